@@ -1,0 +1,252 @@
+"""fp64 CPU oracle for the fused attention operator (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never calls it and shares no code with it.
+
+What it computes is the plain definition, written out with numpy float64,
+one (batch, head) at a time, materialising the whole S_q x S_k score matrix:
+
+* attention: Softmax(Q K^T * scale) V (FlashAttentionScore replacement
+  guide, section 2 "operator math"), with the unfused order of operations
+  of section 4 step 1: scores are scaled first, then the additive mask is
+  added, then softmax, then the product with V;
+* the additive position bias ``pse`` (section 3.2 parameter table) is added
+  after scaling and is not scaled itself; ALiBi is materialised as
+  ``-slope_h * |i - j|``;
+* boolean masks use True = may attend (ops-transformer multimodal
+  FlashAttention page, "Layer 2: cross-modal attention", mask docstring;
+  CogVLM guide, "attention mask": ones then ``tril_``; retrieval page,
+  "Layer 2: semantic modelling": invalid document tokens become -inf).
+  Masked scores are exactly -inf;
+* the per-row log-sum-exp is the natural log and includes scale and bias;
+* a row with no allowed key returns O = 0, LSE = -inf and contributes
+  nothing to any gradient (the pages leave this open: the multimodal page's
+  blockwise code would produce NaN there);
+* the backward is the exact gradient of O with respect to Q, K, V given
+  dO (the guide's section 2 says the fused operator returns gradients
+  without storing the N x N matrix; here that matrix is simply stored,
+  since this is the definition, not the method).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
+closed forms, invariants, finite differences, a library attention routine
+on sliced problems).  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bsh_to_bnsd", "bnsd_to_bsh", "allowed", "bias", "head_scores",
+    "softmax_rows", "attention_fwd", "attention_bwd", "probabilities",
+    "problem_masks", "problem_fwd", "problem_bwd",
+]
+
+
+def bsh_to_bnsd(x: np.ndarray, heads: int) -> np.ndarray:
+    """[B, S, H*D] -> [B, H, S, D]: the head split ``view(B,N,H,D).transpose(1,2)``
+    of the multimodal page's cross-modal attention module."""
+    B, S, HD = x.shape
+    return np.ascontiguousarray(x.reshape(B, S, heads, HD // heads).transpose(0, 2, 1, 3))
+
+
+def bnsd_to_bsh(x: np.ndarray) -> np.ndarray:
+    """[B, H, S, D] -> [B, S, H*D], the inverse of :func:`bsh_to_bnsd`."""
+    B, H, S, D = x.shape
+    return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(B, S, H * D))
+
+
+def allowed(b, h, Sq, Sk, *, causal=False, explicit_mask=None, q_modality=None,
+            k_modality=None, modality_allow=None, modality_allow_diag=False,
+            key_valid=None) -> np.ndarray:
+    """Boolean [Sq, Sk]: may query i of head (b, h) attend to key j.
+
+    The mask kinds combine by AND:
+    * causal: the lower triangle ``tril`` including the diagonal, j <= i
+      (CogVLM guide, attention mask);
+    * explicit: a user bool mask, True = may attend, broadcast over B and H
+      (multimodal page, cross-modal mask [B,N,N] expanded to [B,H,N,N]);
+    * modality: allowed iff allow[m_q(i)][m_k(j)], optionally OR'ed with
+      i == j (the multimodal page's default rule keeps the diagonal);
+    * padding: key j of sample b is a real token (retrieval page doc_mask).
+    """
+    ok = np.ones((Sq, Sk), dtype=bool)
+    if causal:
+        ok &= np.tril(np.ones((Sq, Sk), dtype=bool))
+    if explicit_mask is not None:
+        em = np.asarray(explicit_mask, dtype=bool)
+        if em.ndim == 2:                  # [Sq, Sk]
+            em = em[None, None]
+        elif em.ndim == 3:                # [B, Sq, Sk], shared by every head
+            em = em[:, None]
+        ok &= em[b if em.shape[0] > 1 else 0, h if em.shape[1] > 1 else 0]
+    if q_modality is not None:
+        allow = np.asarray(modality_allow, dtype=bool)
+        qm = np.asarray(q_modality)[b].astype(np.int64)
+        km = np.asarray(k_modality)[b].astype(np.int64)
+        m = allow[qm[:, None], km[None, :]]
+        if modality_allow_diag:
+            m = m | np.eye(Sq, Sk, dtype=bool)
+        ok &= m
+    if key_valid is not None:
+        ok &= np.asarray(key_valid, dtype=bool)[b][None, :]
+    return ok
+
+
+def bias(b, h, Sq, Sk, *, pse=None, alibi_slopes=None) -> np.ndarray | None:
+    """float64 [Sq, Sk] additive bias for head (b, h), or None.
+
+    ``pse`` is a dense tensor broadcastable to [B, H, Sq, Sk]; ALiBi uses
+    -slope_h * |i - j| with the caller's slope values (upcast exactly)."""
+    out = None
+    if pse is not None:
+        p = np.asarray(pse, dtype=np.float64)
+        p = p[b if p.shape[0] > 1 else 0, h if p.shape[1] > 1 else 0]
+        out = np.broadcast_to(p, (Sq, Sk)).astype(np.float64)
+    if alibi_slopes is not None:
+        slope = float(np.asarray(alibi_slopes, dtype=np.float64)[h])
+        i = np.arange(Sq, dtype=np.float64)[:, None]
+        j = np.arange(Sk, dtype=np.float64)[None, :]
+        a = -slope * np.abs(i - j)
+        out = a if out is None else out + a
+    return out
+
+
+def head_scores(q, k, scale, b, h, masks: dict) -> np.ndarray:
+    """Scaled scores plus bias for head (b, h), with disallowed entries set to
+    exactly -inf.  ``q`` [B,H,Sq,D] and ``k`` [B,H,Sk,D] are float64."""
+    Sq, Sk = q.shape[2], k.shape[2]
+    s = scale * (q[b, h] @ k[b, h].T)
+    bb = bias(b, h, Sq, Sk, pse=masks.get("pse"), alibi_slopes=masks.get("alibi_slopes"))
+    if bb is not None:
+        s = s + bb
+    ok = allowed(b, h, Sq, Sk, **{key: masks[key] for key in _MASK_KEYS if key in masks})
+    return np.where(ok, s, -np.inf)
+
+
+_MASK_KEYS = ("causal", "explicit_mask", "q_modality", "k_modality", "modality_allow",
+              "modality_allow_diag", "key_valid")
+
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax of a score matrix that may hold -inf.
+
+    Returns (P, lse): P[i, j] = exp(s_ij - m_i) / sum_j exp(s_ij - m_i) with
+    m_i the row max, and lse_i = m_i + ln(sum_j exp(s_ij - m_i)).  A row whose
+    scores are all -inf gets P = 0 and lse = -inf."""
+    m = s.max(axis=1)
+    dead = ~np.isfinite(m)
+    m_safe = np.where(dead, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    e[dead] = 0.0
+    l = e.sum(axis=1)
+    l_safe = np.where(dead, 1.0, l)
+    P = e / l_safe[:, None]
+    lse = np.where(dead, -np.inf, m_safe + np.log(l_safe))
+    return P, lse
+
+
+def _as_f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):          # a torch tensor: exact upcast
+        import torch
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _as_np(x):
+    if x is None or isinstance(x, (bool, int, float)):
+        return x
+    if hasattr(x, "detach"):
+        return x.detach().cpu().numpy()
+    return np.asarray(x)
+
+
+def _masks(kw) -> dict:
+    out = {}
+    for key, val in kw.items():
+        if val is None:
+            continue
+        if key in ("pse", "alibi_slopes"):
+            out[key] = _as_f64(val)
+        else:
+            out[key] = _as_np(val)
+    return out
+
+
+def probabilities(q, k, scale, b=0, h=0, **masks) -> np.ndarray:
+    """P for head (b, h): the softmax of the masked, biased, scaled scores."""
+    q, k = _as_f64(q), _as_f64(k)
+    P, _ = softmax_rows(head_scores(q, k, scale, b, h, _masks(masks)))
+    return P
+
+
+def attention_fwd(q, k, v, scale, **masks):
+    """O [B,H,Sq,D] and LSE [B,H,Sq], float64, for BNSD inputs.
+
+    O_i = sum_j P_ij v_j with P the row softmax of
+    scale * q_i . k_j + bias_ij over the allowed keys."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    mk = _masks(masks)
+    B, H, Sq, D = q.shape
+    O = np.zeros((B, H, Sq, v.shape[3]), dtype=np.float64)
+    LSE = np.empty((B, H, Sq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            P, lse = softmax_rows(head_scores(q, k, scale, b, h, mk))
+            O[b, h] = P @ v[b, h]
+            LSE[b, h] = lse
+    return O, LSE
+
+
+def attention_bwd(q, k, v, do, scale, **masks):
+    """dQ, dK, dV (float64, BNSD) of L = sum(O * dO).
+
+    With P the forward probabilities:
+    dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  D_i = sum_j P_ij dP_ij;
+    dS_ij = P_ij (dP_ij - D_i);  dQ_i = scale sum_j dS_ij k_j;
+    dK_j = scale sum_i dS_ij q_i.  The bias has no parameters here."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    mk = _masks(masks)
+    B, H = q.shape[:2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            P, _ = softmax_rows(head_scores(q, k, scale, b, h, mk))
+            dv[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            Dl = (P * dP).sum(axis=1)
+            dS = P * (dP - Dl[:, None])
+            dq[b, h] = scale * (dS @ k[b, h])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
+def problem_masks(p) -> dict:
+    """The mask/bias keyword arguments of a problem description (an object
+    with the attributes of ``tiled_attention_03_amd.inputs.Problem``)."""
+    return dict(causal=p.causal, explicit_mask=p.explicit_mask, q_modality=p.q_modality,
+                k_modality=p.k_modality, modality_allow=p.modality_allow,
+                modality_allow_diag=p.modality_allow_diag, key_valid=p.key_valid,
+                pse=p.pse, alibi_slopes=p.alibi_slopes)
+
+
+def _bnsd(x, p):
+    x = _as_f64(x)
+    return bsh_to_bnsd(x, p.heads) if p.layout == "BSH" else x
+
+
+def problem_fwd(p):
+    """(O, LSE) for a problem, O in the problem's own layout (float64)."""
+    O, LSE = attention_fwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), p.scale,
+                           **problem_masks(p))
+    return (bnsd_to_bsh(O) if p.layout == "BSH" else O), LSE
+
+
+def problem_bwd(p):
+    """(dQ, dK, dV) for a problem with upstream gradient ``p.do``, each in the
+    problem's own layout (float64)."""
+    g = attention_bwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), _bnsd(p.do, p), p.scale,
+                      **problem_masks(p))
+    return tuple(bnsd_to_bsh(x) if p.layout == "BSH" else x for x in g)
