@@ -1,0 +1,219 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = one forward (fa_fwd) and one backward (fa_bwd_prep, fa_bwd_main,
+fa_bwd_post) over the long-sequence workload: BNSD bf16, B=1, H=32,
+S=8192, D=128, causal mask plus ALiBi bias, dO ~ N(0,1).  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+Throughput counts algorithmic flops: 4*D per visible (query, key) pair for
+the forward (Q K^T and P V) and 10*D for the backward (the Q K^T recompute,
+dO V^T, P^T dO, dS^T Q, dS K), over the pairs the mask leaves visible.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
+KERNEL_SOURCES = {
+    "fwd": "tiled_attention_03_amd/csrc/fa_fwd.hip",
+    "bwd_main": "tiled_attention_03_amd/csrc/fa_bwd.hip",
+}
+
+
+def visible_pairs(pr) -> int:
+    """Visible (b, h, i, j) pairs left by the workload's mask."""
+    import torch
+    B, H, Sq, Sk = pr.batch, pr.heads, pr.seq_q, pr.seq_k
+    if Sk == 0:
+        return 0
+    total = 0
+    for b in range(B):
+        kv = pr.key_valid[b].bool() if pr.key_valid is not None else torch.ones(Sk, dtype=torch.bool)
+        if pr.q_modality is None and pr.explicit_mask is None:
+            if pr.causal:
+                seen = kv.long().cumsum(0)          # valid keys at or before j
+                total += int(seen[torch.arange(Sq).clamp(max=Sk - 1)].sum()) * H
+            else:
+                total += int(kv.sum()) * Sq * H
+            continue
+        ok = kv[None, :].expand(Sq, Sk).clone()
+        if pr.causal:
+            ok &= torch.ones(Sq, Sk, dtype=torch.bool).tril()
+        if pr.q_modality is not None:
+            allow = pr.modality_allow[pr.q_modality[b].long()][:, pr.k_modality[b].long()]
+            if pr.modality_allow_diag:
+                allow |= torch.eye(Sq, Sk, dtype=torch.bool)
+            ok &= allow
+        if pr.explicit_mask is not None:
+            em = pr.explicit_mask.expand(B, H, Sq, Sk)[b]
+            total += int((ok[None] & em).sum())
+        else:
+            total += int(ok.sum()) * H
+    return total
+
+
+def source_sha(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when the counters were taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(pr, heads=1):
+    """The fp64 oracle timed on this host on a bounded sample of the workload:
+    forward + backward of the first ``heads`` heads at the full sequence."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - reporting only
+        threads = os.cpu_count() or 1
+    sub_q = pr.q[:, :heads].contiguous()
+    sub_k = pr.k[:, :heads].contiguous()
+    sub_v = pr.v[:, :heads].contiguous()
+    sub_do = pr.do[:, :heads].contiguous()
+    slopes = pr.alibi_slopes[:heads].clone()
+    t0 = time.perf_counter()
+    oracle.attention_fwd(sub_q, sub_k, sub_v, pr.scale, causal=pr.causal, alibi_slopes=slopes)
+    oracle.attention_bwd(sub_q, sub_k, sub_v, sub_do, pr.scale, causal=pr.causal,
+                         alibi_slopes=slopes)
+    dt = time.perf_counter() - t0
+    pairs = heads * pr.seq_q * (pr.seq_q + 1) // 2
+    flops = 14 * pr.head_dim * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"fwd+bwd of {heads} of {pr.heads} heads (b=0, h<{heads}) at S={pr.seq_q}, "
+                      f"numpy float64, algorithmic flops 14*D per visible pair"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent: shard heads across GPUs and run this "
+              "per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_attention_03_amd import binding as fa
+    from tiled_attention_03_amd import inputs
+
+    dev = "cuda:0"
+    pr = inputs.config(args.config)
+    q, k, v, do = (t.to(dev) for t in (pr.q, pr.k, pr.v, pr.do))
+    kw = fa.problem_kwargs(pr, dev)
+    plan = fa.Plan(q, k, heads=pr.heads, layout=pr.layout, **kw)
+    o = torch.empty_like(q)
+    lse = torch.empty(pr.batch, pr.heads, pr.seq_q, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    names = ("fwd", "bwd_prep", "bwd_main", "bwd_post")
+
+    def step(ev=None):
+        calls = (lambda: plan.fwd(q, k, v, o, lse),
+                 lambda: plan.bwd_prep(o, do),
+                 lambda: plan.bwd_main(q, k, v, lse, do, dk, dv),
+                 lambda: plan.bwd_post(dq))
+        for n, c in enumerate(calls):
+            if ev is not None:
+                ev[n][0].record()
+            c()
+            if ev is not None:
+                ev[n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in names] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    per = {n: sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+
+    pairs = visible_pairs(pr)
+    D = pr.head_dim
+    f_fwd, f_bwd = 4 * D * pairs, 10 * D * pairs
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = f_fwd / (per["fwd"] * 1e-3) / 1e12
+    bwd_ms = per["bwd_prep"] + per["bwd_main"] + per["bwd_post"]
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    dom = max(("fwd", "bwd_main"), key=lambda n: per[n])
+    dom_flops = f_fwd if dom == "fwd" else f_bwd
+    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    traffic = traffic_for(dom)
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[pr.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": pr.name, "batch": pr.batch, "heads": pr.heads,
+                   "seq_q": pr.seq_q, "seq_k": pr.seq_k, "head_dim": D, "layout": pr.layout,
+                   "causal": pr.causal, "pse": "alibi" if pr.alibi_slopes is not None else None,
+                   "pass": "fwd+bwd", "visible_pairs": pairs},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(per["fwd"], 4), "tflops": round(fwd_tf, 2),
+                "pct_of_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                "pct_of_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)},
+        "kernel_ms": {n: round(per[n], 4) for n in names},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(pr, heads=args.cpu_heads) if args.config == 5 else None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

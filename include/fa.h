@@ -1,0 +1,166 @@
+/* libfa: fused tiled attention for AMD MI355X (gfx950).
+ *
+ * Computes O = Softmax(Q K^T * scale + atten_mask + pse) V and its gradients.
+ *
+ * The operation is the one defined in the FlashAttentionScore replacement
+ * guide (jianzhnie.github.io, "FlashAttentionScore fused-op replacement"):
+ * section 2 gives the formula Softmax(QK^T / sqrt(d_k)) V and states that the
+ * fused operator tiles the work with an online softmax, never storing the
+ * N x N score matrix, and also returns gradients with O(N) extra memory;
+ * section 3.1 gives the call shape (query, key, value, head_num,
+ * input_layout, pse, padding_mask, atten_mask, scale, keep_prob); section 3.2
+ * the parameter meanings (layouts BSH/BNSD, key/value aligned with query,
+ * pse may be ALiBi, the mask may be causal, scale is 1/sqrt(d_k), keep_prob
+ * defaults to 1 = no dropout); section 4 step 1 the unfused order: scores
+ * are scaled, then the additive mask is added, then softmax, then times V.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensor pointers (q, k, v, o, lse, dout, dq, dk, dv, workspace and the mask
+ * and bias arrays inside fa_problem) are DEVICE pointers owned by the caller.
+ * The fa_problem struct itself is host memory read only during the call.
+ * The library allocates no device memory; the backward takes a caller
+ * workspace of fa_bwd_workspace_size() bytes.
+ *
+ * Layouts (element strides; the last dimension is contiguous):
+ *   FA_BNSD: Q/O/dO/dQ [B, H, S_q, D]; K/V/dK/dV [B, H, S_k, D].
+ *   FA_BSH : Q/O/dO/dQ [B, S_q, H*D]; K/V/dK/dV [B, S_k, H*D]; head h owns
+ *            columns [h*D, (h+1)*D), the head split view(B,N,H,D).transpose
+ *            of the multimodal page's cross-modal attention module.
+ * All of Q, K, V, O, dO, dQ, dK, dV share one dtype and one layout.  LSE is
+ * always float32 [B, H, S_q], natural log, and includes scale and bias.
+ *
+ * Masks (bits of mask_flags, combined by AND; a masked score is exactly -inf):
+ *   FA_MASK_CAUSAL   key j visible to query i iff j <= i (top-left aligned
+ *                    lower triangle, the ones/tril_ mask of the CogVLM guide).
+ *   FA_MASK_EXPLICIT uint8 mask, nonzero = may attend, element
+ *                    [b*em_stride_b + h*em_stride_h + i*em_stride_q + j];
+ *                    a zero stride broadcasts that dimension (the multimodal
+ *                    page's [B,N,N] bool mask expanded over heads).
+ *   FA_MASK_MODALITY query i may see key j iff
+ *                    modality_allow[q_modality[b,i] * M + k_modality[b,j]]
+ *                    (or i == j when modality_allow_diag is set: the
+ *                    multimodal page's default rule keeps the diagonal).
+ *                    Modality ids are int8 in [0, M), M <= 8.
+ *   FA_MASK_PADDING  key j of sample b is real iff key_valid[b*S_k + j] != 0
+ *                    (the retrieval page's document mask).
+ * A query row with no visible key gets O = 0, LSE = -inf, and zero gradient.
+ *
+ * Bias (pse, added after scaling, never scaled itself):
+ *   FA_PSE_ALIBI  bias(h,i,j) = -alibi_slopes[h] * |i - j|, slopes float32 [H].
+ *   FA_PSE_DENSE  bias element [b*pse_stride_b + h*pse_stride_h +
+ *                 i*pse_stride_q + j] of dtype pse_dtype (F32, F16 or BF16).
+ *
+ * Errors: every check runs before any launch; a call that fails validation
+ * writes nothing.  FA_ERR_INVALID_ARG: null pointer where one is needed,
+ * negative sizes, H*D mismatch, M out of range, bad enum.
+ * FA_ERR_UNSUPPORTED: keep_prob != 1, a head_dim the kernels do not cover
+ * (F16/BF16: 64 or 128; F32: 32, 64 or 128).  FA_ERR_WORKSPACE: workspace
+ * too small.  FA_ERR_HIP: a HIP launch reported an error.
+ * Sizes of zero are allowed: B, H or S_q == 0 is a no-op; S_k == 0 makes every
+ * row masked (O = 0, LSE = -inf, dQ = 0).
+ *
+ * Synchronisation: calls enqueue work on `stream` and return without waiting.
+ * Outputs are valid once the stream reaches that point.  The library keeps
+ * no mutable global state; calls are thread-safe.  Two calls that write the
+ * same buffers on different streams race, as with any stream work.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,
+  FA_ERR_UNSUPPORTED = -2,
+  FA_ERR_HIP = -3,
+  FA_ERR_WORKSPACE = -4
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+typedef enum { FA_BNSD = 0, FA_BSH = 1 } fa_layout;
+enum {
+  FA_MASK_NONE = 0,
+  FA_MASK_CAUSAL = 1,
+  FA_MASK_EXPLICIT = 2,
+  FA_MASK_MODALITY = 4,
+  FA_MASK_PADDING = 8
+};
+typedef enum { FA_PSE_NONE = 0, FA_PSE_ALIBI = 1, FA_PSE_DENSE = 2 } fa_pse_kind;
+
+/* One attention problem.  Field order is part of the ABI (ctypes mirrors it). */
+typedef struct fa_problem {
+  int32_t batch;            /* B */
+  int32_t head_num;         /* H (head_num of the guide's section 3.1) */
+  int32_t seq_q;            /* S_q */
+  int32_t seq_k;            /* S_k */
+  int32_t head_dim;         /* D; for FA_BSH the hidden size is H*D */
+  int32_t layout;           /* fa_layout */
+  int32_t dtype;            /* fa_dtype of Q, K, V, O, dO, dQ, dK, dV */
+  float scale;              /* multiplies Q K^T; no default (1/sqrt(D) is usual) */
+  float keep_prob;          /* must be 1.0f: dropout is not supported */
+  uint32_t mask_flags;      /* OR of FA_MASK_* */
+  int32_t num_modalities;   /* M, 1..8, for FA_MASK_MODALITY */
+  int32_t modality_allow_diag; /* nonzero: i == j is always allowed */
+  uint8_t modality_allow[64];  /* allow[mq * M + mk], nonzero = allowed */
+  int32_t pse_kind;         /* fa_pse_kind */
+  int32_t pse_dtype;        /* fa_dtype of the dense bias */
+  const uint8_t *explicit_mask;      /* FA_MASK_EXPLICIT */
+  int64_t em_stride_b, em_stride_h, em_stride_q;
+  const int8_t *q_modality;          /* [B, S_q] */
+  const int8_t *k_modality;          /* [B, S_k] */
+  const uint8_t *key_valid;          /* [B, S_k] */
+  const float *alibi_slopes;         /* [H] */
+  const void *pse;                   /* dense bias */
+  int64_t pse_stride_b, pse_stride_h, pse_stride_q;
+} fa_problem;
+
+/* Forward: O (layout/dtype of Q) and LSE (float32 [B,H,S_q]). */
+fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *v,
+                 void *o, float *lse, hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs: float32 dQ accumulator
+ * [B,H,S_q,D] plus float32 row terms D_i = sum_d dO_id * O_id [B,H,S_q],
+ * each rounded up to 256 bytes. */
+fa_status fa_bwd_workspace_size(const fa_problem *p, size_t *bytes);
+
+/* Backward: given Q, K, V, the forward's O and LSE and the upstream dO,
+ * writes dQ, dK, dV (layout/dtype of Q/K/V).  P is recomputed from LSE
+ * (guide section 2: gradients without the N x N matrix).  The three steps
+ * below run in order on `stream`; fa_bwd is exactly their sequence. */
+fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *v,
+                 const void *o, const float *lse, const void *dout,
+                 void *dq, void *dk, void *dv,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward step 1: row terms D_i = sum_d dO_id * O_id into the workspace,
+ * and zeroing of the dQ accumulator. */
+fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward step 2: recompute P per (key tile, query tile) from LSE, write dK
+ * and dV, and accumulate dQ (float32) into the workspace. */
+fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dk, void *dv,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward step 3: dQ = scale * accumulator, converted to dtype/layout. */
+fa_status fa_bwd_post(const fa_problem *p, void *dq, const void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+const char *fa_status_str(fa_status s);
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBFA_FA_H */

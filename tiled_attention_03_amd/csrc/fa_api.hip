@@ -1,0 +1,223 @@
+// C ABI of libfa: argument validation, parameter block, dispatch.
+// The contract of every entry point is documented in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "fa_launch.h"
+
+using namespace fa;
+
+namespace {
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool head_dim_supported(int dtype, int d) {
+  if (dtype == FA_F32) return d == 32 || d == 64 || d == 128;
+  return d == 64 || d == 128;
+}
+
+// True when the problem holds no work at all (B, H or S_q is zero).
+bool empty_problem(const fa_problem *p) {
+  return p->batch == 0 || p->head_num == 0 || p->seq_q == 0;
+}
+
+// Checks everything that does not involve tensor pointers.
+fa_status check_problem(const fa_problem *p) {
+  if (!p) return FA_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->head_num < 0 || p->seq_q < 0 || p->seq_k < 0 || p->head_dim <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (p->layout != FA_BNSD && p->layout != FA_BSH) return FA_ERR_INVALID_ARG;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
+  if (p->keep_prob != 1.0f) return FA_ERR_UNSUPPORTED;
+  if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
+  const uint32_t known = FA_MASK_CAUSAL | FA_MASK_EXPLICIT | FA_MASK_MODALITY | FA_MASK_PADDING;
+  if (p->mask_flags & ~known) return FA_ERR_INVALID_ARG;
+  if (p->pse_kind != FA_PSE_NONE && p->pse_kind != FA_PSE_ALIBI && p->pse_kind != FA_PSE_DENSE)
+    return FA_ERR_INVALID_ARG;
+  // sizes whose indices must fit the kernels' 32-bit row counters
+  const int64_t rows_q = (int64_t)p->batch * p->head_num * p->seq_q;
+  if (rows_q > INT32_MAX || (int64_t)p->head_num * p->head_dim > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (empty_problem(p)) return FA_OK;
+  if (p->mask_flags & FA_MASK_EXPLICIT) {
+    if (!p->explicit_mask) return FA_ERR_INVALID_ARG;
+    if (p->em_stride_b < 0 || p->em_stride_h < 0 || p->em_stride_q < 0) return FA_ERR_INVALID_ARG;
+  }
+  if (p->mask_flags & FA_MASK_MODALITY) {
+    if (!p->q_modality || !p->k_modality) return FA_ERR_INVALID_ARG;
+    if (p->num_modalities < 1 || p->num_modalities > 8) return FA_ERR_INVALID_ARG;
+  }
+  if ((p->mask_flags & FA_MASK_PADDING) && !p->key_valid) return FA_ERR_INVALID_ARG;
+  if (p->pse_kind == FA_PSE_ALIBI && !p->alibi_slopes) return FA_ERR_INVALID_ARG;
+  if (p->pse_kind == FA_PSE_DENSE) {
+    if (!p->pse) return FA_ERR_INVALID_ARG;
+    if (p->pse_dtype != FA_F32 && p->pse_dtype != FA_F16 && p->pse_dtype != FA_BF16)
+      return FA_ERR_INVALID_ARG;
+    if (p->pse_stride_b < 0 || p->pse_stride_h < 0 || p->pse_stride_q < 0)
+      return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+// A tensor pointer that must be present (and 16-byte aligned for vector loads).
+bool tensor_ok(const void *ptr) { return ptr != nullptr && aligned16(ptr); }
+// K/V-shaped tensors may be absent when S_k == 0.
+bool ktensor_ok(const fa_problem *p, const void *ptr) {
+  return p->seq_k == 0 ? (ptr == nullptr || aligned16(ptr)) : tensor_ok(ptr);
+}
+
+Params make_params(const fa_problem *p) {
+  Params r;
+  memset(&r, 0, sizeof(r));
+  const int64_t B = p->batch, H = p->head_num, Sq = p->seq_q, Sk = p->seq_k, D = p->head_dim;
+  r.B = (int)B; r.H = (int)H; r.Sq = (int)Sq; r.Sk = (int)Sk; r.D = (int)D;
+  if (p->layout == FA_BNSD) {
+    r.q_sb = H * Sq * D; r.q_sh = Sq * D; r.q_ss = D;
+    r.k_sb = H * Sk * D; r.k_sh = Sk * D; r.k_ss = D;
+  } else {
+    r.q_sb = Sq * H * D; r.q_sh = D; r.q_ss = H * D;
+    r.k_sb = Sk * H * D; r.k_sh = D; r.k_ss = H * D;
+  }
+  r.scale = p->scale;
+  r.scale_log2 = p->scale * kLog2e;
+  r.mask_flags = p->mask_flags;
+  r.em = p->explicit_mask;
+  r.em_sb = p->em_stride_b; r.em_sh = p->em_stride_h; r.em_sq = p->em_stride_q;
+  r.qmod = p->q_modality; r.kmod = p->k_modality;
+  r.num_modalities = p->num_modalities;
+  r.allow_diag = p->modality_allow_diag != 0;
+  uint64_t bits = 0;
+  if (p->mask_flags & FA_MASK_MODALITY) {
+    const int M = p->num_modalities;
+    for (int a = 0; a < M; ++a)
+      for (int c = 0; c < M; ++c)
+        if (p->modality_allow[a * M + c]) bits |= 1ull << (a * 8 + c);
+  }
+  r.allow_bits = bits;
+  r.key_valid = p->key_valid;
+  r.pse_kind = p->pse_kind;
+  r.pse_dtype = p->pse_dtype;
+  r.alibi_slopes = p->alibi_slopes;
+  r.pse = p->pse;
+  r.pse_sb = p->pse_stride_b; r.pse_sh = p->pse_stride_h; r.pse_sq = p->pse_stride_q;
+  return r;
+}
+
+size_t dq_acc_bytes(const fa_problem *p) {
+  return round256((size_t)p->batch * p->head_num * p->seq_q * p->head_dim * sizeof(float));
+}
+size_t delta_bytes(const fa_problem *p) {
+  return round256((size_t)p->batch * p->head_num * p->seq_q * sizeof(float));
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa_status workspace_ok(const fa_problem *p, const void *ws, size_t bytes) {
+  const size_t need = dq_acc_bytes(p) + delta_bytes(p);
+  if (bytes < need) return FA_ERR_WORKSPACE;
+  if (!tensor_ok(ws)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+void bind_workspace(Params &r, const fa_problem *p, void *ws) {
+  r.dq_acc = (float *)ws;
+  r.delta = (float *)((char *)ws + dq_acc_bytes(p));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char *fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP error";
+    case FA_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *v, void *o,
+                 float *lse, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK || empty_problem(p)) return st;
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse)
+    return FA_ERR_INVALID_ARG;
+  Params r = make_params(p);
+  r.q = q; r.k = k; r.v = v; r.o = o; r.lse = lse;
+  if (p->dtype == FA_F32) return hip_status(launch_fwd_f32(r, stream));
+  return hip_status(launch_fwd_mfma(r, p->dtype, stream));
+}
+
+fa_status fa_bwd_workspace_size(const fa_problem *p, size_t *bytes) {
+  if (!bytes) return FA_ERR_INVALID_ARG;
+  fa_status st = check_problem(p);
+  if (st != FA_OK) return st;
+  *bytes = empty_problem(p) ? 0 : dq_acc_bytes(p) + delta_bytes(p);
+  return FA_OK;
+}
+
+fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK || empty_problem(p)) return st;
+  if (!tensor_ok(o) || !tensor_ok(dout)) return FA_ERR_INVALID_ARG;
+  if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
+  Params r = make_params(p);
+  r.o = (void *)o; r.dout = dout;
+  bind_workspace(r, p, workspace);
+  return hip_status(launch_bwd_prep(r, p->dtype, stream));
+}
+
+fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dk, void *dv, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK || empty_problem(p)) return st;
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !lse || !tensor_ok(dout) ||
+      !ktensor_ok(p, dk) || !ktensor_ok(p, dv))
+    return FA_ERR_INVALID_ARG;
+  if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
+  Params r = make_params(p);
+  r.q = q; r.k = k; r.v = v; r.lse = (float *)lse; r.dout = dout; r.dk = dk; r.dv = dv;
+  bind_workspace(r, p, workspace);
+  if (p->dtype == FA_F32) return hip_status(launch_bwd_f32(r, stream));
+  return hip_status(launch_bwd_mfma(r, p->dtype, stream));
+}
+
+fa_status fa_bwd_post(const fa_problem *p, void *dq, const void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK || empty_problem(p)) return st;
+  if (!tensor_ok(dq)) return FA_ERR_INVALID_ARG;
+  if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
+  Params r = make_params(p);
+  r.dq = dq;
+  bind_workspace(r, p, (void *)workspace);
+  return hip_status(launch_bwd_post(r, p->dtype, stream));
+}
+
+fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *v, const void *o,
+                 const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK || empty_problem(p)) return st;
+  // validate every pointer before the first launch
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse ||
+      !tensor_ok(dout) || !tensor_ok(dq) || !ktensor_ok(p, dk) || !ktensor_ok(p, dv))
+    return FA_ERR_INVALID_ARG;
+  if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
+  if ((st = fa_bwd_prep(p, o, dout, workspace, workspace_bytes, stream)) != FA_OK) return st;
+  if ((st = fa_bwd_main(p, q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, stream)) != FA_OK)
+    return st;
+  return fa_bwd_post(p, dq, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

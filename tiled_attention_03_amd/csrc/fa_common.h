@@ -1,0 +1,126 @@
+// Shared device-side definitions for the libfa kernels (gfx950 only).
+//
+// Parameter block passed by value to every kernel, element conversions, and
+// the per-element mask / bias rules of the operator (see include/fa.h for
+// their definition and sources).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+  // tensors (device pointers)
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const void *dout;
+  void *dq, *dk, *dv;
+  float *dq_acc;   // float32 [B,H,Sq,D]
+  float *delta;    // float32 [B,H,Sq]
+  // element strides: batch, head, row (last dim contiguous)
+  int64_t q_sb, q_sh, q_ss;   // Q, O, dO, dQ
+  int64_t k_sb, k_sh, k_ss;   // K, V, dK, dV
+  int B, H, Sq, Sk, D;
+  float scale;        // multiplies Q K^T
+  float scale_log2;   // scale * log2(e)
+  uint32_t mask_flags;
+  // explicit mask
+  const uint8_t *em;
+  int64_t em_sb, em_sh, em_sq;
+  // modality mask: bit (mq*8 + mk) of allow_bits set = allowed
+  const int8_t *qmod, *kmod;
+  uint64_t allow_bits;
+  int allow_diag;
+  int num_modalities;
+  // padding
+  const uint8_t *key_valid;
+  // bias
+  int pse_kind;
+  int pse_dtype;
+  const float *alibi_slopes;
+  const void *pse;
+  int64_t pse_sb, pse_sh, pse_sq;
+};
+
+// ------------------------------------------------------------------------
+// element conversion
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+template <> __device__ __forceinline__ float to_f32<_Float16>(_Float16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16 / f16 conversions round to nearest even.
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+
+// Two floats -> one dword holding two 16-bit values (lo in bits 0..15), RNE.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------------
+// mask and bias rules, one element at a time (partial tiles only)
+
+__device__ __forceinline__ bool modality_ok(const Params &p, int mq, int mk, int i, int j) {
+  bool ok = (p.allow_bits >> ((unsigned)(mq * 8 + mk))) & 1ull;
+  return ok || (p.allow_diag && i == j);
+}
+
+// Everything except the causal rule and the S_k bound, which the tile loops
+// handle arithmetically.
+__device__ __forceinline__ bool allowed_elem(const Params &p, int b, int h, int i, int j) {
+  const uint32_t f = p.mask_flags;
+  if (f & FA_MASK_CAUSAL) {
+    if (j > i) return false;
+  }
+  if (f & FA_MASK_PADDING) {
+    if (!p.key_valid[(int64_t)b * p.Sk + j]) return false;
+  }
+  if (f & FA_MASK_MODALITY) {
+    int mq = p.qmod[(int64_t)b * p.Sq + i];
+    int mk = p.kmod[(int64_t)b * p.Sk + j];
+    if (!modality_ok(p, mq, mk, i, j)) return false;
+  }
+  if (f & FA_MASK_EXPLICIT) {
+    if (!p.em[(int64_t)b * p.em_sb + (int64_t)h * p.em_sh + (int64_t)i * p.em_sq + j])
+      return false;
+  }
+  return true;
+}
+
+// Dense bias element (natural units, unscaled).
+__device__ __forceinline__ float dense_bias(const Params &p, int b, int h, int i, int j) {
+  int64_t off = (int64_t)b * p.pse_sb + (int64_t)h * p.pse_sh + (int64_t)i * p.pse_sq + j;
+  if (p.pse_dtype == FA_F32) return ((const float *)p.pse)[off];
+  if (p.pse_dtype == FA_BF16) return (float)((const __bf16 *)p.pse)[off];
+  return (float)((const _Float16 *)p.pse)[off];
+}
+
+}  // namespace fa

@@ -1,0 +1,341 @@
+// Forward attention, bf16/f16 inputs, MFMA on gfx950 (CDNA4).
+//
+// What is computed: O = Softmax(Q K^T * scale + mask + pse) V and the row
+// log-sum-exp, tile by tile with an online softmax so the S_q x S_k score
+// matrix never leaves registers (FlashAttentionScore replacement guide,
+// section 2; the tile loop and running statistics are the "tiling + online
+// softmax" of its section 1 and of the NPU FlashAttention study's flow
+// description).
+//
+// Workgroup = NW waves; each wave owns 32 query rows, so BM = 32*NW rows per
+// workgroup share one stream of K/V tiles of BN = 64 keys.  The products are
+// arranged so that a lane owns ONE query row for the whole kernel:
+//
+//   S^T (keys x queries) = K . Q^T     v_mfma_f32_32x32x16, A = K from LDS,
+//                                      B = Q^T kept in VGPRs (loaded once)
+//   O^T (d x queries)   += V^T . P^T   A = V^T from LDS, B = P^T straight
+//                                      from the S^T accumulators
+//
+// With the 32x32 accumulator layout (lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32), lane l holds query l%32 and half of
+// the tile's keys; the other half sits in lane l^32.  Row max and row sum
+// therefore need a single cross-lane exchange per tile, and the running
+// statistics and the O rescale are per-lane scalars.  The P^T operand of
+// the second product is the first product's accumulators rounded to 16 bits
+// in place; V is stored transposed in LDS with the key order inside every
+// 16-key chunk permuted (bits 2 and 3 of the key index swapped) so that each
+// lane's 8 keys sit contiguous and one ds_read_b128 feeds one MFMA operand.
+//
+// Softmax runs in the base-2 domain: t = s * scale * log2(e) + bias * log2(e),
+// p = exp2(t - m); LSE = ln(2) * (m + log2(l)).
+//
+// K/V tiles are double-buffered in LDS: the global loads of tile n+1 are in
+// flight (in VGPRs) while tile n is multiplied; one barrier per tile.
+//
+// Tiles with nothing visible are not visited: the causal rule bounds the
+// tile range, key padding bounds it by the first/last valid key of the
+// sample, and a wave whose 32 rows see none of a tile's keys skips its
+// MFMAs.  Per-element mask work happens only on tiles that need it.
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int BN = 64;  // keys per tile
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<_Float16> {
+  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// Position of key (or query) `u` (0..15) inside its 16-wide chunk in a
+// transposed LDS tile: bits 2 and 3 swapped.
+__device__ __forceinline__ int chunk_pos(int u) {
+  return (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <typename T, int D, int NW>
+struct FwdCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = 32 * NW;
+  static constexpr int KS = D / 16;        // k-steps of Q K^T
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int KP = D + 8;         // K tile pitch (elements)
+  static constexpr int VP = BN + 8;        // V^T tile pitch (elements)
+  static constexpr int KCH = BN * D / 8;   // 16-byte chunks of a K tile
+  static constexpr int KCH_T = (KCH + NT - 1) / NT;
+  static constexpr int VU = (BN / 4) * (D / 8);  // 4-row x 8-col units of a V tile
+  static constexpr int VU_T = (VU + NT - 1) / NT;
+};
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qtiles) {
+  using C = FwdCfg<T, D, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * C::KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VP];
+  __shared__ int kv_range[2];
+
+  const int BH = p.B * p.H;
+  const int lin = blockIdx.x;
+  const int qt = n_qtiles - 1 - lin / BH;   // longest causal rows first
+  const int bh = lin % BH;
+  const int b = bh / p.H, h = bh % p.H;
+  const int q0 = qt * C::BM;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 5, lr = l & 31;
+  const int qw = q0 + 32 * w;
+  const int my_i = qw + lr;
+  const uint32_t flags = p.mask_flags;
+  const bool causal = flags & FA_MASK_CAUSAL;
+
+  const T *Qg = (const T *)p.q + b * p.q_sb + h * p.q_sh;
+  const T *Kg = (const T *)p.k + b * p.k_sb + h * p.k_sh;
+  const T *Vg = (const T *)p.v + b * p.k_sb + h * p.k_sh;
+
+  // ---- key range of this workgroup
+  int k_lo = 0, k_hi = p.Sk;
+  if (causal) k_hi = min(k_hi, q0 + C::BM);
+  if (flags & FA_MASK_PADDING) {
+    if (tid == 0) { kv_range[0] = p.Sk; kv_range[1] = 0; }
+    __syncthreads();
+    int lo = p.Sk, hi = 0;
+    const uint8_t *kv = p.key_valid + (int64_t)b * p.Sk;
+    for (int j = tid; j < p.Sk; j += C::NT) {
+      if (kv[j]) { lo = min(lo, j); hi = max(hi, j + 1); }
+    }
+    atomicMin(&kv_range[0], lo);
+    atomicMax(&kv_range[1], hi);
+    __syncthreads();
+    k_lo = max(k_lo, kv_range[0]);
+    k_hi = min(k_hi, kv_range[1]);
+  }
+  const int kt_begin = k_lo / BN;
+  const int kt_end = k_hi > k_lo ? (k_hi + BN - 1) / BN : kt_begin;
+
+  // ---- Q^T fragments (B operand), one row per lane, loaded once
+  u32x4 qf[C::KS];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) {
+    if (my_i < p.Sq)
+      qf[t] = *(const u32x4 *)(Qg + (int64_t)my_i * p.q_ss + 16 * t + 8 * g);
+    else
+      qf[t] = u32x4{0, 0, 0, 0};
+  }
+
+  const float sl2 = (p.pse_kind == FA_PSE_ALIBI) ? p.alibi_slopes[h] * kLog2e : 0.f;
+  const bool elem_mask_any = flags & (FA_MASK_PADDING | FA_MASK_MODALITY | FA_MASK_EXPLICIT);
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- global -> register prefetch of one K/V tile
+  u32x4 kreg[C::KCH_T];
+  u32x4 vreg[C::VU_T][4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BN;
+#pragma unroll
+    for (int it = 0; it < C::KCH_T; ++it) {
+      const int c = tid + it * C::NT;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      if (c < C::KCH && k0 + row < p.Sk)
+        kreg[it] = *(const u32x4 *)(Kg + (int64_t)(k0 + row) * p.k_ss + col8 * 8);
+      else
+        kreg[it] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < C::VU_T; ++it) {
+      const int u = tid + it * C::NT;
+      const int j4 = u % (BN / 4), col8 = u / (BN / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = k0 + 4 * j4 + r;
+        if (u < C::VU && row < p.Sk)
+          vreg[it][r] = *(const u32x4 *)(Vg + (int64_t)row * p.k_ss + col8 * 8);
+        else
+          vreg[it][r] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < C::KCH_T; ++it) {
+      const int c = tid + it * C::NT;
+      const int row = c / (D / 8), col8 = c % (D / 8);
+      if (c < C::KCH) *(u32x4 *)(&Ks[buf][row * C::KP + col8 * 8]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VU_T; ++it) {
+      const int u = tid + it * C::NT;
+      if (u >= C::VU) continue;
+      const int j4 = u % (BN / 4), col8 = u / (BN / 4);
+      const int pos = 16 * (j4 >> 2) + chunk_pos(4 * (j4 & 3));
+      uint16_t *dst = &Vt[buf][(col8 * 8) * C::VP + pos];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t a0 = vreg[it][0][e2], a1 = vreg[it][1][e2];
+        const uint32_t a2 = vreg[it][2][e2], a3 = vreg[it][3][e2];
+        *(u32x2 *)(dst + (2 * e2) * C::VP) = u32x2{lo_halves(a0, a1), lo_halves(a2, a3)};
+        *(u32x2 *)(dst + (2 * e2 + 1) * C::VP) = u32x2{hi_halves(a0, a1), hi_halves(a2, a3)};
+      }
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    gload(kt_begin);
+    sstore(0);
+  }
+  __syncthreads();
+
+  int cur = 0;
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) gload(kt + 1);
+    const int k0 = kt * BN;
+
+    // wave-level tile classification
+    bool skip = my_i - lr >= p.Sq;  // whole wave past the last query row
+    bool need_mask = elem_mask_any || (k0 + BN > p.Sk);
+    if (causal) {
+      if (k0 > qw + 31) skip = true;
+      if (k0 + BN - 1 > qw) need_mask = true;
+    }
+    if (!skip) {
+      const uint16_t *ks = Ks[cur];
+      const uint16_t *vt = Vt[cur];
+      // S^T = K . Q^T for two 32-key blocks
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int t = 0; t < C::KS; ++t) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const u32x4 a = *(const u32x4 *)(ks + (32 * jb + lr) * C::KP + 16 * t + 8 * g);
+          s[jb] = Mfma<T>::mac(a, qf[t], s[jb]);
+        }
+      }
+      // scores -> base-2 logits with bias and mask
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+          float t = s[jb][r] * p.scale_log2;
+          if (p.pse_kind == FA_PSE_ALIBI) t -= sl2 * fabsf((float)(my_i - j));
+          else if (p.pse_kind == FA_PSE_DENSE && my_i < p.Sq && j < p.Sk)
+            t += dense_bias(p, b, h, my_i, j) * kLog2e;
+          if (need_mask) {
+            bool ok = j < p.Sk && my_i < p.Sq;
+            if (ok) ok = allowed_elem(p, b, h, my_i, j);
+            if (!ok) t = -INFINITY;
+          }
+          s[jb][r] = t;
+          mx = fmaxf(mx, t);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_fast(s[jb][r] - m_use);
+          s[jb][r] = e;
+          rs += e;
+        }
+      }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      // O^T += V^T . P^T over four 16-key chunks
+#pragma unroll
+      for (int c = 0; c < BN / 16; ++c) {
+        const int jb = c >> 1, r0 = 8 * (c & 1);
+        u32x4 pk;
+        pk[0] = pack2<T>(s[jb][r0 + 0], s[jb][r0 + 1]);
+        pk[1] = pack2<T>(s[jb][r0 + 2], s[jb][r0 + 3]);
+        pk[2] = pack2<T>(s[jb][r0 + 4], s[jb][r0 + 5]);
+        pk[3] = pack2<T>(s[jb][r0 + 6], s[jb][r0 + 7]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const u32x4 a = *(const u32x4 *)(vt + (32 * db + lr) * C::VP + 16 * c + 8 * g);
+          acc[db] = Mfma<T>::mac(a, pk, acc[db]);
+        }
+      }
+    }
+    if (has_next) sstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---- epilogue: O = acc / l, LSE
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (my_i < p.Sq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    T *Og = (T *)p.o + b * p.q_sb + h * p.q_sh + (int64_t)my_i * p.q_ss;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        u32x2 v;
+        v[0] = pack2<T>(acc[db][4 * rr + 0] * inv, acc[db][4 * rr + 1] * inv);
+        v[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
+        *(u32x2 *)(Og + d0) = v;
+      }
+    }
+    if (g == 0)
+      p.lse[((int64_t)b * p.H + h) * p.Sq + my_i] =
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_t(const Params &p, hipStream_t s) {
+  using C = FwdCfg<T, D, NW>;
+  const int n_qtiles = (p.Sq + C::BM - 1) / C::BM;
+  const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(C::NT), 0, s, p,
+                     n_qtiles);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(const Params &p, hipStream_t s) {
+  const bool small_q = p.Sq <= 32;
+  if (p.D == 64) return small_q ? launch_t<T, 64, 1>(p, s) : launch_t<T, 64, 4>(p, s);
+  if (p.D == 128) return small_q ? launch_t<T, 128, 1>(p, s) : launch_t<T, 128, 4>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const Params &p, int dtype, hipStream_t s) {
+  if (dtype == FA_BF16) return launch_dtype<__bf16>(p, s);
+  if (dtype == FA_F16) return launch_dtype<_Float16>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa
