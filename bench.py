@@ -115,8 +115,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(every (batch, head) is independent: shard heads across GPUs and run this "

@@ -38,6 +38,15 @@ fa_status check_problem(const fa_problem *p) {
   if (p->mask_flags & ~known) return FA_ERR_INVALID_ARG;
   if (p->pse_kind != FA_PSE_NONE && p->pse_kind != FA_PSE_ALIBI && p->pse_kind != FA_PSE_DENSE)
     return FA_ERR_INVALID_ARG;
+  // one (batch, head) span of Q/K-shaped tensors must stay below 2 GiB: the
+  // kernels address it with 32-bit byte offsets
+  {
+    const int64_t es = p->dtype == FA_F32 ? 4 : 2;
+    const int64_t hd = (int64_t)p->head_num * p->head_dim;
+    const int64_t rs = p->layout == FA_BSH ? hd : p->head_dim;
+    const int64_t span_q = ((int64_t)p->seq_q * rs) * es, span_k = ((int64_t)p->seq_k * rs) * es;
+    if (span_q >= ((int64_t)1 << 31) || span_k >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  }
   // sizes whose indices must fit the kernels' 32-bit row counters
   const int64_t rows_q = (int64_t)p->batch * p->head_num * p->seq_q;
   if (rows_q > INT32_MAX || (int64_t)p->head_num * p->head_dim > INT32_MAX) return FA_ERR_UNSUPPORTED;

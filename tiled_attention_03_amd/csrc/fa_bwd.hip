@@ -265,15 +265,18 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(Params p, int n_ktiles
         dSs[il * C::SP + 32 * w + lr] = 0;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dQ(block) += dS . K over this wave's key chunks, column block dbq
     {
-      f32x16 dq = f32x16{};
+      f32x16 dq0 = f32x16{}, dq1 = f32x16{};   // two independent MFMA chains
 #pragma unroll
-      for (int c = 0; c < C::NCH; ++c) {
-        const u32x4 a = *(const u32x4 *)(&dSs[lr * C::SP + 16 * (c0 + c) + 8 * g]);
-        dq = MfmaB<T>::mac(a, ktf[c], dq);
+      for (int c = 0; c < C::NCH; c += 2) {
+        const u32x4 a0 = *(const u32x4 *)(&dSs[lr * C::SP + 16 * (c0 + c) + 8 * g]);
+        const u32x4 a1 = *(const u32x4 *)(&dSs[lr * C::SP + 16 * (c0 + c + 1) + 8 * g]);
+        dq0 = MfmaB<T>::mac(a0, ktf[c], dq0);
+        dq1 = MfmaB<T>::mac(a1, ktf[c + 1], dq1);
       }
+      const f32x16 dq = dq0 + dq1;
       float *dst = p.dq_acc + (rbase + i0) * D + 32 * dbq + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(Params p, int n_ktiles
       }
     }
     if (has_next) sstore();
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- write dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr

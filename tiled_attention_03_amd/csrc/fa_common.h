@@ -85,6 +85,29 @@ template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float lo, float 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros (no fault), which is how tile tails are zero-filled.  Offsets
+// are 32-bit, so callers keep one (batch, head) span below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+// Bytes spanned by `rows` rows of `d` elements at row stride `stride` elements.
+__device__ __forceinline__ uint32_t span_bytes(int rows, int64_t stride, int d, int esize) {
+  return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * stride + d) * esize) : 0u;
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete before it arrives, so after the barrier every wave sees every
+// other wave's LDS writes.  Outstanding global loads, stores and atomics are
+// not waited for (a plain __syncthreads() fence would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------------------
 // mask and bias rules, one element at a time (partial tiles only)
 

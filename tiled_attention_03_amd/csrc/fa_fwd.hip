@@ -41,7 +41,9 @@
 namespace fa {
 namespace {
 
-constexpr int BN = 64;  // keys per tile
+constexpr int BN = 64;          // keys per tile
+constexpr int kMaxTiles = 512;  // key-tile summaries kept in LDS (S_k <= 32768)
+constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
 
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * C::KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VP];
   __shared__ int kv_range[2];
+  __shared__ uint32_t tsum[kMaxTiles];  // per key tile: bits 0-7 modality set of valid keys,
+                                        // bit 8 some key invalid or past S_k
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
@@ -128,18 +132,61 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   const int kt_begin = k_lo / BN;
   const int kt_end = k_hi > k_lo ? (k_hi + BN - 1) / BN : kt_begin;
 
-  // ---- Q^T fragments (B operand), one row per lane, loaded once
+  constexpr int ES = (int)sizeof(T);
+  const auto Qr = make_rsrc(Qg, span_bytes(p.Sq, p.q_ss, D, ES));
+  const auto Kr = make_rsrc(Kg, span_bytes(p.Sk, p.k_ss, D, ES));
+  const auto Vr = make_rsrc(Vg, span_bytes(p.Sk, p.k_ss, D, ES));
+  const uint32_t krow_b = (uint32_t)(p.k_ss * ES);   // bytes between K/V rows
+
+  // ---- Q^T fragments (B operand), one row per lane, loaded once (rows past
+  // S_q read as zeros)
   u32x4 qf[C::KS];
+  {
+    const uint32_t qoff = my_i < p.Sq ? (uint32_t)((int64_t)my_i * p.q_ss * ES) : 0x80000000u;
 #pragma unroll
-  for (int t = 0; t < C::KS; ++t) {
-    if (my_i < p.Sq)
-      qf[t] = *(const u32x4 *)(Qg + (int64_t)my_i * p.q_ss + 16 * t + 8 * g);
-    else
-      qf[t] = u32x4{0, 0, 0, 0};
+    for (int t = 0; t < C::KS; ++t) qf[t] = buf_load16(Qr, qoff + (16 * t + 8 * g) * ES);
   }
 
-  const float sl2 = (p.pse_kind == FA_PSE_ALIBI) ? p.alibi_slopes[h] * kLog2e : 0.f;
-  const bool elem_mask_any = flags & (FA_MASK_PADDING | FA_MASK_MODALITY | FA_MASK_EXPLICIT);
+  const bool alibi = p.pse_kind == FA_PSE_ALIBI;
+  const bool dense = p.pse_kind == FA_PSE_DENSE;
+  const float c_log2 = p.scale_log2;
+  const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;   // slope in log2 units
+  const float sl2c = alibi ? sl2 / c_log2 : 0.f;                 // slope in raw-score units
+  const bool f_pad = flags & FA_MASK_PADDING, f_mod = flags & FA_MASK_MODALITY;
+  const bool f_exp = flags & FA_MASK_EXPLICIT;
+
+  // ---- per key tile summaries (padding / modality), one wave-wide vote per tile
+  const int n_kt_all = (p.Sk + BN - 1) / BN;
+  const bool use_summary = (f_pad || f_mod) && n_kt_all <= kMaxTiles;
+  uint32_t allow_any = 0, allow_all = 0xffu;   // over the modalities of this wave's rows
+  if (use_summary) {
+    for (int kt = w; kt < n_kt_all; kt += NW) {
+      const int j = kt * BN + l;
+      bool valid = j < p.Sk;
+      int m = 0;
+      if (valid && f_pad) valid = p.key_valid[(int64_t)b * p.Sk + j] != 0;
+      if (valid && f_mod) m = p.kmod[(int64_t)b * p.Sk + j];
+      uint32_t bits = __ballot(!valid) ? 0x100u : 0u;
+      if (f_mod) {
+        for (int mm = 0; mm < p.num_modalities; ++mm)
+          if (__ballot(valid && m == mm)) bits |= 1u << mm;
+      } else if (__ballot(valid)) {
+        bits |= 1u;
+      }
+      if (l == 0) tsum[kt] = bits;
+    }
+    if (f_mod) {
+      const int mq = my_i < p.Sq ? p.qmod[(int64_t)b * p.Sq + my_i] : -1;
+      for (int mm = 0; mm < p.num_modalities; ++mm) {
+        if (__ballot(mq == mm)) {
+          const uint32_t row = (uint32_t)(p.allow_bits >> (8 * mm)) & 0xffu;
+          allow_any |= row;
+          allow_all &= row;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -149,28 +196,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   // ---- global -> register prefetch of one K/V tile
   u32x4 kreg[C::KCH_T];
   u32x4 vreg[C::VU_T][4];
+  // rows past S_k read as zeros through the buffer range check
   auto gload = [&](int kt) {
-    const int k0 = kt * BN;
+    const uint32_t base = (uint32_t)kt * BN * krow_b;
 #pragma unroll
     for (int it = 0; it < C::KCH_T; ++it) {
       const int c = tid + it * C::NT;
       const int row = c / (D / 8), col8 = c % (D / 8);
-      if (c < C::KCH && k0 + row < p.Sk)
-        kreg[it] = *(const u32x4 *)(Kg + (int64_t)(k0 + row) * p.k_ss + col8 * 8);
-      else
-        kreg[it] = u32x4{0, 0, 0, 0};
+      if (C::KCH % C::NT == 0 || c < C::KCH)
+        kreg[it] = buf_load16(Kr, base + row * krow_b + col8 * 16);
     }
 #pragma unroll
     for (int it = 0; it < C::VU_T; ++it) {
       const int u = tid + it * C::NT;
       const int j4 = u % (BN / 4), col8 = u / (BN / 4);
+      if (C::VU % C::NT == 0 || u < C::VU) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = k0 + 4 * j4 + r;
-        if (u < C::VU && row < p.Sk)
-          vreg[it][r] = *(const u32x4 *)(Vg + (int64_t)row * p.k_ss + col8 * 8);
-        else
-          vreg[it][r] = u32x4{0, 0, 0, 0};
+        for (int r = 0; r < 4; ++r)
+          vreg[it][r] = buf_load16(Vr, base + (4 * j4 + r) * krow_b + col8 * 16);
       }
     }
   };
@@ -210,13 +253,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     if (has_next) gload(kt + 1);
     const int k0 = kt * BN;
 
-    // wave-level tile classification
-    bool skip = my_i - lr >= p.Sq;  // whole wave past the last query row
-    bool need_mask = elem_mask_any || (k0 + BN > p.Sk);
+    // ---- wave-level tile class: skip, fast (no per-element work) or general
+    bool skip = qw >= p.Sq;
+    bool general = dense || f_exp || (k0 + BN > p.Sk);
     if (causal) {
       if (k0 > qw + 31) skip = true;
-      if (k0 + BN - 1 > qw) need_mask = true;
+      else if (k0 + BN - 1 > qw) general = true;
     }
+    int adir = 0;   // ALiBi on a tile wholly below (+1) or above (-1) the diagonal
+    if (alibi) {
+      if (k0 + BN - 1 <= qw) adir = 1;
+      else if (k0 >= qw + 31) adir = -1;
+      else general = true;
+    }
+    if (use_summary) {
+      const uint32_t ts = tsum[kt];
+      const uint32_t kset = ts & 0xffu;
+      if (f_mod) {
+        const bool diag = p.allow_diag && k0 < qw + 32 && k0 + BN > qw;
+        if ((kset & allow_any) == 0 && !diag) skip = true;
+        if ((kset & ~allow_all) != 0 || diag) general = true;
+      } else if (kset == 0) {
+        skip = true;
+      }
+      if (ts & 0x100u) general = true;
+    } else if (f_pad || f_mod) {
+      general = true;
+    }
+
     if (!skip) {
       const uint16_t *ks = Ks[cur];
       const uint16_t *vt = Vt[cur];
@@ -230,44 +294,72 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
           s[jb] = Mfma<T>::mac(a, qf[t], s[jb]);
         }
       }
-      // scores -> base-2 logits with bias and mask
-      float mx = -INFINITY;
+      // Logit of element r of block jb is  t = cs * s + lane_off  (base-2 units).
+      // Fast tiles: cs = scale*log2(e), the ALiBi term split into a per-register
+      // constant (folded into s) and a per-lane constant lane_off.
+      // General tiles: s already holds t (cs = 1, lane_off = 0), -inf where masked.
+      float cs = c_log2, lane_off = 0.f, mx = -INFINITY;
+      if (!general) {
+        if (adir != 0) {
+          const float a = adir * sl2c;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+          for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-          float t = s[jb][r] * p.scale_log2;
-          if (p.pse_kind == FA_PSE_ALIBI) t -= sl2 * fabsf((float)(my_i - j));
-          else if (p.pse_kind == FA_PSE_DENSE && my_i < p.Sq && j < p.Sk)
-            t += dense_bias(p, b, h, my_i, j) * kLog2e;
-          if (need_mask) {
+            for (int r = 0; r < 16; ++r)
+              s[jb][r] = fmaf(a, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), s[jb][r]);
+          lane_off = adir * sl2 * (float)(k0 + 4 * g - my_i);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+        mx = fmaf(mx, cs, lane_off);
+      } else {
+        cs = 1.f;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+            float t = s[jb][r] * c_log2;
             bool ok = j < p.Sk && my_i < p.Sq;
             if (ok) ok = allowed_elem(p, b, h, my_i, j);
-            if (!ok) t = -INFINITY;
+            if (ok) {
+              if (alibi) t -= sl2 * fabsf((float)(my_i - j));
+              else if (dense) t += dense_bias(p, b, h, my_i, j) * kLog2e;
+            } else {
+              t = -INFINITY;
+            }
+            s[jb][r] = t;
+            mx = fmaxf(mx, t);
           }
-          s[jb][r] = t;
-          mx = fmaxf(mx, t);
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
+      // lazy rescale: the reference max moves only when a row max grows by > kTau;
+      // exp2(t - m_run) then stays <= 2^kTau and O, l share the same reference.
+      const bool grow = mx > m_run + kTau;
+      float alpha = 1.f;
+      if (grow) {
+        alpha = exp2_fast(m_run - mx);
+        m_run = mx;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      }
+      const float off = lane_off - (m_run == -INFINITY ? 0.f : m_run);
       float rs = 0.f;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(s[jb][r] - m_use);
+          const float e = exp2_fast(fmaf(s[jb][r], cs, off));
           s[jb][r] = e;
           rs += e;
         }
       }
       l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
       // O^T += V^T . P^T over four 16-key chunks
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c) {
@@ -285,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
       }
     }
     if (has_next) sstore(cur ^ 1);
-    __syncthreads();
+    lds_barrier();
     cur ^= 1;
   }
 
