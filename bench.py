@@ -28,6 +28,7 @@ METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 KERNEL_SOURCES = {
     "fwd": "tiled_attention_03_amd/csrc/fa_fwd.hip",
     "bwd_main": "tiled_attention_03_amd/csrc/fa_bwd.hip",
+    "bwd_post": "tiled_attention_03_amd/csrc/fa_bwd.hip",
 }
 
 
@@ -155,7 +156,7 @@ def main():
         calls = (lambda: plan.fwd(q, k, v, o, lse),
                  lambda: plan.bwd_prep(o, do),
                  lambda: plan.bwd_main(q, k, v, lse, do, dk, dv),
-                 lambda: plan.bwd_post(dq))
+                 lambda: plan.bwd_post(q, k, v, lse, do, dq))
         for n, c in enumerate(calls):
             if ev is not None:
                 ev[n][0].record()

@@ -128,34 +128,37 @@ typedef struct fa_problem {
 fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *v,
                  void *o, float *lse, hipStream_t stream);
 
-/* Bytes of device workspace fa_bwd needs: float32 dQ accumulator
- * [B,H,S_q,D] plus float32 row terms D_i = sum_d dO_id * O_id [B,H,S_q],
- * each rounded up to 256 bytes. */
+/* Bytes of device workspace fa_bwd needs: the float32 row terms
+ * D_i = sum_d dO_id * O_id, [B,H,S_q], rounded up to 256 bytes. */
 fa_status fa_bwd_workspace_size(const fa_problem *p, size_t *bytes);
 
 /* Backward: given Q, K, V, the forward's O and LSE and the upstream dO,
- * writes dQ, dK, dV (layout/dtype of Q/K/V).  P is recomputed from LSE
- * (guide section 2: gradients without the N x N matrix).  The three steps
- * below run in order on `stream`; fa_bwd is exactly their sequence. */
+ * writes dQ, dK, dV (layout/dtype of Q/K/V) of L = sum(O * dO).  P is
+ * recomputed tile by tile from LSE (guide section 2: gradients without the
+ * N x N matrix).  No atomics are used: the result is bitwise repeatable.
+ * fa_bwd is exactly the sequence of the three steps below on `stream`. */
 fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *v,
                  const void *o, const float *lse, const void *dout,
                  void *dq, void *dk, void *dv,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Backward step 1: row terms D_i = sum_d dO_id * O_id into the workspace,
- * and zeroing of the dQ accumulator. */
+/* Backward step 1: row terms D_i = sum_d dO_id * O_id into the workspace. */
 fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Backward step 2: recompute P per (key tile, query tile) from LSE, write dK
- * and dV, and accumulate dQ (float32) into the workspace. */
+/* Backward step 2 (key-tile pass): for each key tile, recompute P and dS over
+ * the query tiles that see it and write dV = P^T dO and dK = scale dS^T Q.
+ * Reads the row terms of step 1 from the workspace. */
 fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const void *v,
                       const float *lse, const void *dout, void *dk, void *dv,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+                      const void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Backward step 3: dQ = scale * accumulator, converted to dtype/layout. */
-fa_status fa_bwd_post(const fa_problem *p, void *dq, const void *workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+/* Backward step 3 (query-tile pass): for each query tile, recompute P and dS
+ * over the key tiles it sees and write dQ = scale dS K.  Reads the row terms
+ * of step 1 from the workspace; independent of step 2. */
+fa_status fa_bwd_post(const fa_problem *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dq,
+                      const void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 const char *fa_status_str(fa_status s);
 int fa_abi_version(void);

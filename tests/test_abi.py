@@ -115,13 +115,13 @@ def test_workspace_size_and_checks():
     n = ctypes.c_size_t(0)
     assert fa.lib.fa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     r256 = lambda x: (x + 255) // 256 * 256
-    assert n.value == r256(3 * 5 * 77 * 128 * 4) + r256(3 * 5 * 77 * 4)
+    assert n.value == r256(3 * 5 * 77 * 4)
     assert fa.lib.fa_bwd_workspace_size(ctypes.byref(p), None) == fa.FA_ERR_INVALID_ARG
     # too small a workspace is refused before any launch
     st = fa.lib.fa_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                        FAKE, n.value - 1, None)
     assert st == fa.FA_ERR_WORKSPACE
-    st = fa.lib.fa_bwd_post(ctypes.byref(p), FAKE, FAKE, 16, None)
+    st = fa.lib.fa_bwd_post(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert st == fa.FA_ERR_WORKSPACE
     st = fa.lib.fa_bwd_prep(ctypes.byref(base_problem(keep_prob=0.5)), FAKE, FAKE, FAKE, 1 << 30,
                             None)

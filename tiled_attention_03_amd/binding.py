@@ -82,7 +82,7 @@ def _load():
         "fa_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "fa_bwd_prep": [P, vp, vp, vp, sz, vp],
         "fa_bwd_main": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "fa_bwd_post": [P, vp, vp, sz, vp],
+        "fa_bwd_post": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -276,8 +276,8 @@ def bwd(q, k, v, o, lse, do, *, heads: int, layout: str = "BNSD", workspace=None
 
 class Plan:
     """A prepared problem: the struct is built once and the four device calls
-    (fwd, bwd prep, bwd main, bwd post) can be issued repeatedly, e.g. by a
-    benchmark that brackets each call with events."""
+    (fwd; bwd prep = row terms, bwd main = dK/dV, bwd post = dQ) can be issued
+    repeatedly, e.g. by a benchmark that brackets each call with events."""
 
     def __init__(self, q, k, *, heads: int, layout: str = "BNSD", **kw):
         self.p, self._keep = make_problem(q, k, heads=heads, layout=layout, **kw)
@@ -298,9 +298,9 @@ class Plan:
         _check(lib.fa_bwd_main(self._pp, _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk),
                                _ptr(dv), _ptr(self.ws), self.ws.numel(), _stream()), "fa_bwd_main")
 
-    def bwd_post(self, dq):
-        _check(lib.fa_bwd_post(self._pp, _ptr(dq), _ptr(self.ws), self.ws.numel(), _stream()),
-               "fa_bwd_post")
+    def bwd_post(self, q, k, v, lse, do, dq):
+        _check(lib.fa_bwd_post(self._pp, _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq),
+                               _ptr(self.ws), self.ws.numel(), _stream()), "fa_bwd_post")
 
 
 def problem_kwargs(pr, device) -> dict:

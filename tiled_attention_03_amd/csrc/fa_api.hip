@@ -115,9 +115,6 @@ Params make_params(const fa_problem *p) {
   return r;
 }
 
-size_t dq_acc_bytes(const fa_problem *p) {
-  return round256((size_t)p->batch * p->head_num * p->seq_q * p->head_dim * sizeof(float));
-}
 size_t delta_bytes(const fa_problem *p) {
   return round256((size_t)p->batch * p->head_num * p->seq_q * sizeof(float));
 }
@@ -125,16 +122,12 @@ size_t delta_bytes(const fa_problem *p) {
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 fa_status workspace_ok(const fa_problem *p, const void *ws, size_t bytes) {
-  const size_t need = dq_acc_bytes(p) + delta_bytes(p);
-  if (bytes < need) return FA_ERR_WORKSPACE;
+  if (bytes < delta_bytes(p)) return FA_ERR_WORKSPACE;
   if (!tensor_ok(ws)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
-void bind_workspace(Params &r, const fa_problem *p, void *ws) {
-  r.dq_acc = (float *)ws;
-  r.delta = (float *)((char *)ws + dq_acc_bytes(p));
-}
+void bind_workspace(Params &r, void *ws) { r.delta = (float *)ws; }
 
 }  // namespace
 
@@ -169,7 +162,7 @@ fa_status fa_bwd_workspace_size(const fa_problem *p, size_t *bytes) {
   if (!bytes) return FA_ERR_INVALID_ARG;
   fa_status st = check_problem(p);
   if (st != FA_OK) return st;
-  *bytes = empty_problem(p) ? 0 : dq_acc_bytes(p) + delta_bytes(p);
+  *bytes = empty_problem(p) ? 0 : delta_bytes(p);
   return FA_OK;
 }
 
@@ -181,13 +174,13 @@ fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout, void
   if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
   Params r = make_params(p);
   r.o = (void *)o; r.dout = dout;
-  bind_workspace(r, p, workspace);
+  bind_workspace(r, workspace);
   return hip_status(launch_bwd_prep(r, p->dtype, stream));
 }
 
 fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const void *v,
-                      const float *lse, const void *dout, void *dk, void *dv, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      const float *lse, const void *dout, void *dk, void *dv,
+                      const void *workspace, size_t workspace_bytes, hipStream_t stream) {
   fa_status st = check_problem(p);
   if (st != FA_OK || empty_problem(p)) return st;
   if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !lse || !tensor_ok(dout) ||
@@ -196,21 +189,25 @@ fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const v
   if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
   Params r = make_params(p);
   r.q = q; r.k = k; r.v = v; r.lse = (float *)lse; r.dout = dout; r.dk = dk; r.dv = dv;
-  bind_workspace(r, p, workspace);
-  if (p->dtype == FA_F32) return hip_status(launch_bwd_f32(r, stream));
-  return hip_status(launch_bwd_mfma(r, p->dtype, stream));
+  bind_workspace(r, (void *)workspace);
+  if (p->dtype == FA_F32) return hip_status(launch_bwd_kv_f32(r, stream));
+  return hip_status(launch_bwd_kv_mfma(r, p->dtype, stream));
 }
 
-fa_status fa_bwd_post(const fa_problem *p, void *dq, const void *workspace,
+fa_status fa_bwd_post(const fa_problem *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dq, const void *workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   fa_status st = check_problem(p);
   if (st != FA_OK || empty_problem(p)) return st;
-  if (!tensor_ok(dq)) return FA_ERR_INVALID_ARG;
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !lse || !tensor_ok(dout) ||
+      !tensor_ok(dq))
+    return FA_ERR_INVALID_ARG;
   if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
   Params r = make_params(p);
-  r.dq = dq;
-  bind_workspace(r, p, (void *)workspace);
-  return hip_status(launch_bwd_post(r, p->dtype, stream));
+  r.q = q; r.k = k; r.v = v; r.lse = (float *)lse; r.dout = dout; r.dq = dq;
+  bind_workspace(r, (void *)workspace);
+  if (p->dtype == FA_F32) return hip_status(launch_bwd_q_f32(r, stream));
+  return hip_status(launch_bwd_q_mfma(r, p->dtype, stream));
 }
 
 fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *v, const void *o,
@@ -226,7 +223,7 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
   if ((st = fa_bwd_prep(p, o, dout, workspace, workspace_bytes, stream)) != FA_OK) return st;
   if ((st = fa_bwd_main(p, q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, stream)) != FA_OK)
     return st;
-  return fa_bwd_post(p, dq, workspace, workspace_bytes, stream);
+  return fa_bwd_post(p, q, k, v, lse, dout, dq, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

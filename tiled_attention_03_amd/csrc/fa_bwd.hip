@@ -1,298 +1,214 @@
 // Backward attention, bf16/f16 inputs, MFMA on gfx950.
 //
 // Recompute-based gradient (FlashAttentionScore replacement guide, section
-// 2: gradients are formed without the N x N matrix, from O(N) saved
-// statistics).  Only O and the row LSE come from the forward; every P tile is
-// recomputed as P = exp2(S * scale * log2 e + bias * log2 e - LSE * log2 e).
+// 2: gradients come without the N x N matrix, from O(N) saved statistics).
+// Only O and the row LSE come from the forward; every P tile is recomputed
+// as P = exp2(S * scale * log2 e + bias * log2 e - LSE * log2 e), and
+// dS = P * (dP - delta) with delta_i = sum_d dO_id O_id (the prep pass).
 //
-// Workgroup = 4 waves owning BNB = 128 consecutive keys (32 per wave) of one
-// (batch, head); it walks the query blocks of 32 rows that can see those keys
-// (causal: from the diagonal down).  Per query block, per wave:
+// Two passes, no atomics, bitwise repeatable:
 //
-//   S  = Q  . K^T    A = Q  tile (LDS, row-major)    B = K rows (VGPRs)
-//   dP = dO . V^T    A = dO tile (LDS, row-major)    B = V rows (VGPRs)
-//   P  = exp2(...), dS = P * (dP - delta_i)          (fp32, in registers)
-//   dV += P^T . dO   A = P^T from the S accumulators B = dO^T tile (LDS)
-//   dK += dS^T . Q   A = dS^T from registers         B = Q^T tile (LDS)
-//   dQ  = dS . K     A = dS of all 128 keys (LDS)    B = K^T (VGPRs)
+// * key pass (dK, dV): a workgroup of 4 waves owns 128 keys of one
+//   (batch, head), 32 per wave, and walks the 32-row query blocks that can
+//   see them (causal: from the diagonal down).  Per block and wave:
+//     S  = Q . K^T,  dP = dO . V^T  (A = Q / dO rows from LDS, B = the wave's
+//                                    K / V rows held in VGPRs)
+//     dV += P^T . dO, dK += dS^T . Q (A = P^T / dS^T straight from the S / dP
+//                                    accumulators, B = transposed LDS reads)
+//   In the 32x32 accumulator layout a lane holds one key and 16 queries,
+//   which is exactly the A layout of P^T and dS^T with queries as the
+//   contraction index, so those never move.
 //
-// In the 32x32 accumulator layout lane l holds key l%32 of the wave and 16
-// query rows, which is exactly the A-operand layout of P^T / dS^T for the dV
-// and dK products (keys as rows, queries as the contraction index), so those
-// two need no data movement.  dQ contracts over keys instead, so dS goes
-// through LDS once; each wave then forms dQ for one 32-column block of D over
-// the workgroup's keys and adds it to the float32 accumulator with hardware
-// float atomics.  Q^T and dO^T tiles use the same bits-2-and-3 swapped
-// position order inside each 16-row chunk as the forward's V^T tile.
+// * query pass (dQ): a workgroup of 4 waves owns 128 query rows (32 per wave)
+//   and walks the 64-key tiles they can see, like the forward:
+//     S^T = K . Q^T, dP^T = V . dO^T (A = K / V rows from LDS, B = Q / dO rows
+//                                    of the lane's query, in VGPRs)
+//     dQ^T += K^T . dS^T             (A = transposed K reads, B = dS^T from
+//                                    the accumulators)
+//   A lane owns one query row, so LSE and delta are per-lane scalars.
+//
+// Both passes double-buffer their streamed tiles in LDS: the tiles of step
+// n+1 are loaded from global memory straight into LDS (no register staging)
+// while step n is multiplied, with one barrier per step; blocks the mask hides
+// entirely are skipped.
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
 
-constexpr int NWB = 4;      // waves per workgroup
-constexpr int BNB = 128;    // keys per workgroup
-constexpr int BMB = 32;     // queries per iteration
+constexpr int NWB = 4;      // waves per workgroup (both passes)
+constexpr int KB = 128;     // keys per workgroup, key pass
+constexpr int QB = 32;      // queries per step, key pass
+constexpr int QBQ = 128;    // queries per workgroup, query pass
+constexpr int KBQ = 64;     // keys per step, query pass
 
-template <typename T> struct MfmaB;
-template <> struct MfmaB<__bf16> {
-  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-};
-template <> struct MfmaB<_Float16> {
-  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-};
-
-__device__ __forceinline__ int chunk_pos_b(int u) {
-  return (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
-}
-__device__ __forceinline__ uint32_t lo_h(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_h(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
-template <int D>
-struct BwdCfg {
-  static constexpr int NT = NWB * 64;
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int QP = D + 8;      // row-major Q / dO tile pitch
-  static constexpr int TP = BMB + 8;    // transposed tile pitch
-  static constexpr int SP = BNB + 8;    // dS tile pitch
-  static constexpr int WPD = NWB / DB;  // waves sharing one dQ column block
-  static constexpr int NCH = (BNB / 16) / WPD;  // 16-key chunks per wave for dQ
-  static constexpr int UNITS = (BMB / 4) * (D / 8);  // 4-row x 8-col units per tile
-};
-
+// ===========================================================================
+// key pass: dK, dV
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(Params p, int n_ktiles) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BMB * C::QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[BMB * C::QP];
-  __shared__ __attribute__((aligned(16))) uint16_t QTs[D * C::TP];
-  __shared__ __attribute__((aligned(16))) uint16_t GTs[D * C::TP];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[BMB * C::SP];
-  __shared__ float lse_s[BMB], dlt_s[BMB];
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) {
+  constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
+  constexpr int ES = (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][QB * D];
+  __shared__ __attribute__((aligned(16))) float lam_s[2][QB];   // LSE*log2e (+ALiBi row term)
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QB];   // LSE*log2e
+  __shared__ __attribute__((aligned(16))) float dlt_s[2][QB];
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
-  const int kt = lin / BH;          // key tile 0 has the most causal work: first
+  const int kt = lin / BH;            // key tile 0 sees the most causal rows: first
   const int bh = lin % BH;
   const int b = bh / p.H, h = bh % p.H;
-  const int j0 = kt * BNB;
+  const int j0 = kt * KB;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g = l >> 5, lr = l & 31;
   const int jw = j0 + 32 * w;
   const int my_j = jw + lr;
   const uint32_t flags = p.mask_flags;
   const bool causal = flags & FA_MASK_CAUSAL;
-  const bool elem_mask_any = flags & (FA_MASK_PADDING | FA_MASK_MODALITY | FA_MASK_EXPLICIT);
+  const bool alibi = p.pse_kind == FA_PSE_ALIBI, dense = p.pse_kind == FA_PSE_DENSE;
+  const bool f_elem = flags & (FA_MASK_PADDING | FA_MASK_MODALITY | FA_MASK_EXPLICIT);
 
   const int64_t qoff = b * p.q_sb + h * p.q_sh;
   const int64_t koff = b * p.k_sb + h * p.k_sh;
-  const T *Qg = (const T *)p.q + qoff;
-  const T *Gg = (const T *)p.dout + qoff;
-  const T *Kg = (const T *)p.k + koff;
-  const T *Vg = (const T *)p.v + koff;
+  const auto Qr = make_rsrc((const T *)p.q + qoff, span_bytes(p.Sq, p.q_ss, D, ES));
+  const auto Gr = make_rsrc((const T *)p.dout + qoff, span_bytes(p.Sq, p.q_ss, D, ES));
+  const auto Kr = make_rsrc((const T *)p.k + koff, span_bytes(p.Sk, p.k_ss, D, ES));
+  const auto Vr = make_rsrc((const T *)p.v + koff, span_bytes(p.Sk, p.k_ss, D, ES));
+  const uint32_t qrow_b = (uint32_t)(p.q_ss * ES);
   const int64_t rbase = ((int64_t)b * p.H + h) * p.Sq;
 
-  // ---- resident operands: K and V rows of this lane's key, K^T for dQ
-  u32x4 kf[C::KS], vf[C::KS];
+  // K and V rows of this lane's key: B operands of Q K^T and dO V^T
+  u32x4 kf[KS], vf[KS];
+  {
+    const uint32_t off = my_j < p.Sk ? (uint32_t)((int64_t)my_j * p.k_ss * ES) : 0x80000000u;
 #pragma unroll
-  for (int t = 0; t < C::KS; ++t) {
-    if (my_j < p.Sk) {
-      kf[t] = *(const u32x4 *)(Kg + (int64_t)my_j * p.k_ss + 16 * t + 8 * g);
-      vf[t] = *(const u32x4 *)(Vg + (int64_t)my_j * p.k_ss + 16 * t + 8 * g);
-    } else {
-      kf[t] = vf[t] = u32x4{0, 0, 0, 0};
+    for (int t = 0; t < KS; ++t) {
+      kf[t] = buf_load16(Kr, off + (16 * t + 8 * g) * ES);
+      vf[t] = buf_load16(Vr, off + (16 * t + 8 * g) * ES);
     }
   }
-  const int dbq = w % C::DB;                 // dQ column block of this wave
-  const int c0 = (w / C::DB) * C::NCH;       // first 16-key chunk of this wave for dQ
-  u32x4 ktf[C::NCH];
+  f32x16 dv[DB], dk[DB];
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c) {
-    uint16_t e[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int j = j0 + 16 * (c0 + c) + 8 * g + s;
-      e[s] = (j < p.Sk) ? ((const uint16_t *)Kg)[(int64_t)j * p.k_ss + 32 * dbq + lr] : 0;
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ktf[c][s] = (uint32_t)e[2 * s] | ((uint32_t)e[2 * s + 1] << 16);
-  }
+  for (int db = 0; db < DB; ++db) dv[db] = dk[db] = f32x16{};
 
-  f32x16 dv[C::DB], dk[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) dv[db] = dk[db] = f32x16{};
+  const float c_log2 = p.scale_log2;
+  const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
 
-  const float sl2 = (p.pse_kind == FA_PSE_ALIBI) ? p.alibi_slopes[h] * kLog2e : 0.f;
+  const int it_begin = causal ? (j0 / QB) : 0;
+  const int it_end = (p.Sq + QB - 1) / QB;
 
-  // query blocks that can see this key tile
-  const int it_begin = causal ? (j0 / BMB) : 0;
-  const int it_end = (p.Sq + BMB - 1) / BMB;
-
-  // ---- staging of one query block: Q, dO row-major and transposed, LSE, delta
-  u32x4 ld[4];
-  auto gload = [&](int it) {
-    const int i0 = it * BMB;
-    const int u = tid % C::UNITS;
-    const int which = tid / C::UNITS;  // 0: Q, 1: dO, else idle
-    const int i4 = u / (D / 8), col8 = u % (D / 8);
-    const T *src = which == 0 ? Qg : Gg;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * i4 + r;
-      if (which < 2 && i < p.Sq)
-        ld[r] = *(const u32x4 *)(src + (int64_t)i * p.q_ss + col8 * 8);
-      else
-        ld[r] = u32x4{0, 0, 0, 0};
-    }
-  };
-  float ls_reg = 0.f;
-  auto gload_stats = [&](int it) {
-    const int i = it * BMB + (tid & 31);
-    if (tid < 32) {
+  // staging: Q and dO tiles go straight to LDS (rows past S_q read as zeros);
+  // LSE and delta of the block pass through 32 lanes' registers.
+  float st_lse = 0.f, st_dlt = 0.f;
+  auto gload = [&](int it, int buf) {
+    const uint32_t base = (uint32_t)it * QB * qrow_b;
+    tile_load_lds<D, QB, NWB>(Qs[buf], Qr, base, qrow_b, w, l);
+    tile_load_lds<D, QB, NWB>(Gs[buf], Gr, base, qrow_b, w, l);
+    if (tid < QB) {
+      const int i = it * QB + tid;
       const float v = i < p.Sq ? p.lse[rbase + i] : -INFINITY;
-      ls_reg = (v == -INFINITY) ? INFINITY : v * kLog2e;   // dead rows: P = 0
-    } else if (tid < 64) {
-      ls_reg = i < p.Sq ? p.delta[rbase + i] : 0.f;
+      st_lse = (v == -INFINITY) ? INFINITY : v * kLog2e;   // dead rows give P = 0
+      st_dlt = i < p.Sq ? p.delta[rbase + i] : 0.f;
     }
   };
-  auto sstore = [&]() {
-    const int u = tid % C::UNITS;
-    const int which = tid / C::UNITS;
-    if (which < 2) {
-      const int i4 = u / (D / 8), col8 = u % (D / 8);
-      uint16_t *nat = which == 0 ? Qs : Gs;
-      uint16_t *tr = which == 0 ? QTs : GTs;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4 *)(&nat[(4 * i4 + r) * C::QP + col8 * 8]) = ld[r];
-      const int pos = 16 * (i4 >> 2) + chunk_pos_b(4 * (i4 & 3));
-      uint16_t *dst = &tr[(col8 * 8) * C::TP + pos];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t a0 = ld[0][e2], a1 = ld[1][e2], a2 = ld[2][e2], a3 = ld[3][e2];
-        *(u32x2 *)(dst + (2 * e2) * C::TP) = u32x2{lo_h(a0, a1), lo_h(a2, a3)};
-        *(u32x2 *)(dst + (2 * e2 + 1) * C::TP) = u32x2{hi_h(a0, a1), hi_h(a2, a3)};
-      }
+  auto sstore = [&](int buf) {
+    if (tid < QB) {
+      lse_s[buf][tid] = st_lse;
+      lam_s[buf][tid] = st_lse + sl2 * (float)tid;
+      dlt_s[buf][tid] = st_dlt;
     }
-    if (tid < 32) lse_s[tid] = ls_reg;
-    else if (tid < 64) dlt_s[tid - 32] = ls_reg;
   };
 
   if (it_begin < it_end) {
-    gload(it_begin);
-    gload_stats(it_begin);
-    sstore();
+    gload(it_begin, 0);
+    sstore(0);
   }
-  __syncthreads();
+  vm_wait_barrier();
 
+  int cur = 0;
   for (int it = it_begin; it < it_end; ++it) {
     const bool has_next = it + 1 < it_end;
-    if (has_next) {
-      gload(it + 1);
-      gload_stats(it + 1);
-    }
-    const int i0 = it * BMB;
-    // wave-level classification of this (query block, 32 keys) tile
-    bool skip = jw >= p.Sk;
-    bool need_mask = elem_mask_any || (jw + 32 > p.Sk) || (i0 + BMB > p.Sq);
-    if (causal) {
-      if (jw > i0 + BMB - 1) skip = true;
-      if (jw + 31 > i0) need_mask = true;
-    }
-    if (!skip) {
+    if (has_next) gload(it + 1, cur ^ 1);
+    const int i0 = it * QB;
+    // wave-level class of the (32 queries x 32 keys) block: fast (no
+    // per-element work) or general.  Blocks the mask hides wholly are rare
+    // here (a few per workgroup) and take the general path, which yields
+    // P = dS = 0; keeping the accumulation unconditional lets the dK/dV
+    // accumulators stay in place across iterations.
+    bool general = f_elem || dense || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
+    if (causal && jw + 31 > i0) general = true;
+    if (alibi && !(i0 >= jw + 31)) general = true;   // fast ALiBi form needs i >= j
+    {
+      const uint16_t *qs = Qs[cur];
+      const uint16_t *gs = Gs[cur];
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
-        const u32x4 aq = *(const u32x4 *)(&Qs[lr * C::QP + 16 * t + 8 * g]);
-        const u32x4 ag = *(const u32x4 *)(&Gs[lr * C::QP + 16 * t + 8 * g]);
-        s = MfmaB<T>::mac(aq, kf[t], s);
-        dp = MfmaB<T>::mac(ag, vf[t], dp);
+      for (int t = 0; t < KS; ++t) {
+        s = Mfma<T>::mac(read_row<D>(qs, lr, 2 * t + g), kf[t], s);
+        dp = Mfma<T>::mac(read_row<D>(gs, lr, 2 * t + g), vf[t], dp);
       }
-      // P and dS; element r: query i0 + 8(r/4) + 4g + r%4, key my_j
+      // element r: query i0 + il, il = 8(r/4) + 4g + r%4; key my_j
+      if (!general) {
+        const float L = sl2 * (float)(my_j - i0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 8 * (r >> 2) + 4 * g + (r & 3);
-        const int i = i0 + il;
-        float t = s[r] * p.scale_log2;
-        if (p.pse_kind == FA_PSE_ALIBI) t -= sl2 * fabsf((float)(i - my_j));
-        else if (p.pse_kind == FA_PSE_DENSE && i < p.Sq && my_j < p.Sk)
-          t += dense_bias(p, b, h, i, my_j) * kLog2e;
-        float pr = exp2_fast(t - lse_s[il]);
-        if (need_mask) {
-          bool ok = i < p.Sq && my_j < p.Sk;
-          if (ok) ok = allowed_elem(p, b, h, i, my_j);
-          if (!ok) pr = 0.f;
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 lam = *(const f32x4 *)&lam_s[cur][8 * rr + 4 * g];
+          const f32x4 dl = *(const f32x4 *)&dlt_s[cur][8 * rr + 4 * g];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * rr + q;
+            const float pr = exp2_fast(fmaf(s[r], c_log2, L - lam[q]));
+            s[r] = pr;
+            dp[r] = pr * (dp[r] - dl[q]);
+          }
         }
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - dlt_s[il]);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 ls = *(const f32x4 *)&lse_s[cur][8 * rr + 4 * g];
+          const f32x4 dl = *(const f32x4 *)&dlt_s[cur][8 * rr + 4 * g];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * rr + q;
+            const int i = i0 + 8 * rr + 4 * g + q;
+            bool ok = i < p.Sq && my_j < p.Sk;
+            if (ok) ok = allowed_elem(p, b, h, i, my_j);
+            float pr = 0.f;
+            if (ok) {
+              float t = s[r] * c_log2;
+              if (alibi) t -= sl2 * fabsf((float)(i - my_j));
+              else if (dense) t += dense_bias(p, b, h, i, my_j) * kLog2e;
+              pr = exp2_fast(t - ls[q]);
+            }
+            s[r] = pr;
+            dp[r] = pr * (dp[r] - dl[q]);
+          }
+        }
       }
-      // dV += P^T dO, dK += dS^T Q (contraction over the 32 queries)
+      // dV += P^T dO, dK += dS^T Q, contraction over the 32 queries
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int r0 = 8 * c;
-        u32x4 pp, pd;
+        const u32x4 pp = pack8<T>(s, 8 * c);
+        const u32x4 pd = pack8<T>(dp, 8 * c);
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          pp[q2] = pack2<T>(s[r0 + 2 * q2], s[r0 + 2 * q2 + 1]);
-          pd[q2] = pack2<T>(dp[r0 + 2 * q2], dp[r0 + 2 * q2 + 1]);
-        }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const u32x4 bg = *(const u32x4 *)(&GTs[(32 * db + lr) * C::TP + 16 * c + 8 * g]);
-          const u32x4 bq = *(const u32x4 *)(&QTs[(32 * db + lr) * C::TP + 16 * c + 8 * g]);
-          dv[db] = MfmaB<T>::mac(pp, bg, dv[db]);
-          dk[db] = MfmaB<T>::mac(pd, bq, dk[db]);
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = Mfma<T>::mac(pp, read_tr<D>(gs, 0, c, 32 * db, l), dv[db]);
+          dk[db] = Mfma<T>::mac(pd, read_tr<D>(qs, 0, c, 32 * db, l), dk[db]);
         }
       }
-      // dS (rounded) to LDS, row = query, column = key of the workgroup
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 8 * (r >> 2) + 4 * g + (r & 3);
-        const uint32_t v = pack2<T>(dp[r], 0.f);
-        dSs[il * C::SP + 32 * w + lr] = (uint16_t)(v & 0xffffu);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 8 * (r >> 2) + 4 * g + (r & 3);
-        dSs[il * C::SP + 32 * w + lr] = 0;
-      }
     }
-    lds_barrier();
-    // dQ(block) += dS . K over this wave's key chunks, column block dbq
-    {
-      f32x16 dq0 = f32x16{}, dq1 = f32x16{};   // two independent MFMA chains
-#pragma unroll
-      for (int c = 0; c < C::NCH; c += 2) {
-        const u32x4 a0 = *(const u32x4 *)(&dSs[lr * C::SP + 16 * (c0 + c) + 8 * g]);
-        const u32x4 a1 = *(const u32x4 *)(&dSs[lr * C::SP + 16 * (c0 + c + 1) + 8 * g]);
-        dq0 = MfmaB<T>::mac(a0, ktf[c], dq0);
-        dq1 = MfmaB<T>::mac(a1, ktf[c + 1], dq1);
-      }
-      const f32x16 dq = dq0 + dq1;
-      float *dst = p.dq_acc + (rbase + i0) * D + 32 * dbq + lr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (i0 + il < p.Sq) unsafeAtomicAdd(dst + (int64_t)il * D, dq[r]);
-      }
-    }
-    if (has_next) sstore();
-    lds_barrier();
+    if (has_next) sstore(cur ^ 1);
+    vm_wait_barrier();
+    cur ^= 1;
   }
 
-  // ---- write dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
+  // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
   T *DKg = (T *)p.dk + koff;
   T *DVg = (T *)p.dv + koff;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = jw + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -304,25 +220,198 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(Params p, int n_ktiles
   }
 }
 
+// ===========================================================================
+// query pass: dQ
 template <typename T, int D>
-hipError_t launch_t(const Params &p, hipStream_t s) {
-  const int n_ktiles = (p.Sk + BNB - 1) / BNB;
+__global__ __launch_bounds__(256, 1) void bwd_q_kernel(Params p, int n_qtiles) {
+  constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
+  constexpr int ES = (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KBQ * D];
+
+  const int BH = p.B * p.H;
+  const int lin = blockIdx.x;
+  const int qt = n_qtiles - 1 - lin / BH;   // longest causal rows first
+  const int bh = lin % BH;
+  const int b = bh / p.H, h = bh % p.H;
+  const int q0 = qt * QBQ;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 5, lr = l & 31;
+  const int qw = q0 + 32 * w;
+  const int my_i = qw + lr;
+  const uint32_t flags = p.mask_flags;
+  const bool causal = flags & FA_MASK_CAUSAL;
+  const bool alibi = p.pse_kind == FA_PSE_ALIBI, dense = p.pse_kind == FA_PSE_DENSE;
+  const bool f_elem = flags & (FA_MASK_PADDING | FA_MASK_MODALITY | FA_MASK_EXPLICIT);
+
+  const int64_t qoff = b * p.q_sb + h * p.q_sh;
+  const int64_t koff = b * p.k_sb + h * p.k_sh;
+  const auto Qr = make_rsrc((const T *)p.q + qoff, span_bytes(p.Sq, p.q_ss, D, ES));
+  const auto Gr = make_rsrc((const T *)p.dout + qoff, span_bytes(p.Sq, p.q_ss, D, ES));
+  const auto Kr = make_rsrc((const T *)p.k + koff, span_bytes(p.Sk, p.k_ss, D, ES));
+  const auto Vr = make_rsrc((const T *)p.v + koff, span_bytes(p.Sk, p.k_ss, D, ES));
+  const uint32_t krow_b = (uint32_t)(p.k_ss * ES);
+  const int64_t rbase = ((int64_t)b * p.H + h) * p.Sq;
+
+  // this lane's query row: Q and dO as B operands, LSE and delta
+  u32x4 qf[KS], gf[KS];
+  {
+    const uint32_t off = my_i < p.Sq ? (uint32_t)((int64_t)my_i * p.q_ss * ES) : 0x80000000u;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      qf[t] = buf_load16(Qr, off + (16 * t + 8 * g) * ES);
+      gf[t] = buf_load16(Gr, off + (16 * t + 8 * g) * ES);
+    }
+  }
+  float lse2 = INFINITY, dlt = 0.f;
+  if (my_i < p.Sq) {
+    const float v = p.lse[rbase + my_i];
+    lse2 = (v == -INFINITY) ? INFINITY : v * kLog2e;
+    dlt = p.delta[rbase + my_i];
+  }
+
+  const float c_log2 = p.scale_log2;
+  const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
+  const float sl2c = alibi ? sl2 / c_log2 : 0.f;
+
+  int k_hi = p.Sk;
+  if (causal) k_hi = min(k_hi, q0 + QBQ);
+  const int kt_end = (k_hi + KBQ - 1) / KBQ;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // K and V tiles go straight to LDS; rows past S_k read as zeros
+  auto gload = [&](int kt, int buf) {
+    const uint32_t base = (uint32_t)kt * KBQ * krow_b;
+    tile_load_lds<D, KBQ, NWB>(Ks[buf], Kr, base, krow_b, w, l);
+    tile_load_lds<D, KBQ, NWB>(Vs[buf], Vr, base, krow_b, w, l);
+  };
+
+  if (kt_end > 0) gload(0, 0);
+  vm_wait_barrier();
+
+  int cur = 0;
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) gload(kt + 1, cur ^ 1);
+    const int k0 = kt * KBQ;
+    // fast or general tile; tiles hidden from this wave (at most one per
+    // workgroup on the causal diagonal) take the general path (dS = 0) so the
+    // accumulation stays unconditional
+    bool general = f_elem || dense || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq);
+    if (causal && k0 + KBQ - 1 > qw) general = true;
+    if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
+    {
+      const uint16_t *ks = Ks[cur];
+      const uint16_t *vs = Vs[cur];
+      const float off = (alibi ? sl2 * (float)(k0 + 4 * g - my_i) : 0.f) - lse2;
+      // one 32-key block at a time (LSE is known: no row max to wait for)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          s = Mfma<T>::mac(read_row<D>(ks, 32 * jb + lr, 2 * t + g), qf[t], s);
+          dp = Mfma<T>::mac(read_row<D>(vs, 32 * jb + lr, 2 * t + g), gf[t], dp);
+        }
+        // element r: key k0 + 32jb + 8(r/4) + 4g + r%4, query my_i
+        if (!general) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float u = s[r];
+            if (alibi) u = fmaf(sl2c, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), u);
+            const float pr = exp2_fast(fmaf(u, c_log2, off));
+            dp[r] = pr * (dp[r] - dlt);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+            bool ok = j < p.Sk && my_i < p.Sq;
+            if (ok) ok = allowed_elem(p, b, h, my_i, j);
+            float pr = 0.f;
+            if (ok) {
+              float t = s[r] * c_log2;
+              if (alibi) t -= sl2 * fabsf((float)(my_i - j));
+              else if (dense) t += dense_bias(p, b, h, my_i, j) * kLog2e;
+              pr = exp2_fast(t - lse2);
+            }
+            dp[r] = pr * (dp[r] - dlt);
+          }
+        }
+        // dQ^T += K^T . dS^T over this block's two 16-key chunks
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const u32x4 pd = pack8<T>(dp, 8 * hh);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = Mfma<T>::mac(read_tr<D>(ks, 0, 2 * jb + hh, 32 * db, l), pd, acc[db]);
+        }
+      }
+    }
+    vm_wait_barrier();
+    cur ^= 1;
+  }
+
+  // dQ = scale * acc; element (db, r): column 32db + 8(r/4) + 4g + r%4
+  if (my_i < p.Sq) {
+    T *Dg = (T *)p.dq + qoff + (int64_t)my_i * p.q_ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        u32x2 v;
+        v[0] = pack2<T>(acc[db][4 * rr + 0] * p.scale, acc[db][4 * rr + 1] * p.scale);
+        v[1] = pack2<T>(acc[db][4 * rr + 2] * p.scale, acc[db][4 * rr + 3] * p.scale);
+        *(u32x2 *)(Dg + d0) = v;
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_kv(const Params &p, hipStream_t s) {
+  const int n_ktiles = (p.Sk + KB - 1) / KB;
   const int64_t blocks = (int64_t)n_ktiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_mfma_kernel<T, D>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s, p,
+  hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s, p,
                      n_ktiles);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_q(const Params &p, hipStream_t s) {
+  const int n_qtiles = (p.Sq + QBQ - 1) / QBQ;
+  const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_q_kernel<T, D>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s, p,
+                     n_qtiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_mfma(const Params &p, int dtype, hipStream_t s) {
+hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s) {
   if (dtype == FA_BF16) {
-    if (p.D == 64) return launch_t<__bf16, 64>(p, s);
-    if (p.D == 128) return launch_t<__bf16, 128>(p, s);
+    if (p.D == 64) return launch_kv<__bf16, 64>(p, s);
+    if (p.D == 128) return launch_kv<__bf16, 128>(p, s);
   } else if (dtype == FA_F16) {
-    if (p.D == 64) return launch_t<_Float16, 64>(p, s);
-    if (p.D == 128) return launch_t<_Float16, 128>(p, s);
+    if (p.D == 64) return launch_kv<_Float16, 64>(p, s);
+    if (p.D == 128) return launch_kv<_Float16, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s) {
+  if (dtype == FA_BF16) {
+    if (p.D == 64) return launch_q<__bf16, 64>(p, s);
+    if (p.D == 128) return launch_q<__bf16, 128>(p, s);
+  } else if (dtype == FA_F16) {
+    if (p.D == 64) return launch_q<_Float16, 64>(p, s);
+    if (p.D == 128) return launch_q<_Float16, 128>(p, s);
   }
   return hipErrorInvalidValue;
 }

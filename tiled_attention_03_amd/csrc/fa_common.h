@@ -29,8 +29,7 @@ struct Params {
   float *lse;
   const void *dout;
   void *dq, *dk, *dv;
-  float *dq_acc;   // float32 [B,H,Sq,D]
-  float *delta;    // float32 [B,H,Sq]
+  float *delta;    // float32 [B,H,Sq]: delta_i = sum_d dO_id O_id
   // element strides: batch, head, row (last dim contiguous)
   int64_t q_sb, q_sh, q_ss;   // Q, O, dO, dQ
   int64_t k_sb, k_sh, k_ss;   // K, V, dK, dV

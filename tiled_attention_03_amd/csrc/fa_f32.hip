@@ -1,4 +1,4 @@
-// fp32 attention path and the dtype-generic backward prep/post passes.
+// fp32 attention path and the dtype-generic backward prep pass.
 //
 // The fp32 path keeps every product and sum in fp32 FMA (no bf16/xf32
 // shortcut).  One query row (forward, dQ) or one key row (dK/dV) is owned by
@@ -12,6 +12,7 @@
 // stored.  Backward: P is recomputed from the saved LSE, then
 // dP = dO.v, dS = P (dP - delta), dQ += dS k (query-owned kernel) and
 // dV += P dO, dK += dS q (key-owned kernel): no atomics, deterministic.
+// The prep pass forms delta_i = sum_d dO_id O_id for every dtype.
 #include "fa_launch.h"
 
 namespace fa {
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Params p) {
   }
 }
 
-// dQ (unscaled) into dq_acc, one query row per lane group.
+// dQ = scale * sum_j dS_ij k_j, one query row per lane group.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(Params p) {
   constexpr int TPR = RowSplit<D>::TPR, ROWS = RowSplit<D>::ROWS;
@@ -151,9 +152,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(Params p) {
     }
   }
   if (i < p.Sq) {
-    float *out = p.dq_acc + row * D + part * 32;
+    float *out = (float *)p.dq + b * p.q_sb + h * p.q_sh + (int64_t)i * p.q_ss + part * 32;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) out[e] = acc[e];
+    for (int e = 0; e < 32; ++e) out[e] = acc[e] * p.scale;
   }
 }
 
@@ -240,27 +241,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Params p) {
     const T *G = (const T *)p.dout + off;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(to_f32<T>(O[e]), to_f32<T>(G[e]), acc);
-    float *z = p.dq_acc + row * p.D + part * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = 0.f;
   }
   for (int off = 1; off < lanes_per_row; off <<= 1) acc += __shfl_xor(acc, off, 64);
   if (i < p.Sq && part == 0) p.delta[row] = acc;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_post_kernel(Params p) {
-  const int lanes_per_row = p.D / 8;
-  const int rows_per_block = 256 / lanes_per_row;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
-  const int i = blockIdx.x * rows_per_block + threadIdx.x / lanes_per_row;
-  const int part = threadIdx.x % lanes_per_row;
-  if (i >= p.Sq) return;
-  const int64_t row = ((int64_t)b * p.H + h) * p.Sq + i;
-  const float *src = p.dq_acc + row * p.D + part * 8;
-  T *dst = (T *)p.dq + b * p.q_sb + h * p.q_sh + (int64_t)i * p.q_ss + part * 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = from_f32<T>(src[e] * p.scale);
 }
 
 template <int D>
@@ -271,22 +254,25 @@ hipError_t fwd_f32_d(const Params &p, hipStream_t s) {
 }
 
 template <int D>
-hipError_t bwd_f32_d(const Params &p, hipStream_t s) {
-  dim3 gq((p.Sq + RowSplit<D>::ROWS - 1) / RowSplit<D>::ROWS, p.B * p.H);
-  hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, gq, dim3(256), 0, s, p);
-  if (p.Sk > 0) {
-    dim3 gk((p.Sk + RowSplit<D>::ROWS - 1) / RowSplit<D>::ROWS, p.B * p.H);
-    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, gk, dim3(256), 0, s, p);
-  }
+hipError_t bwd_kv_f32_d(const Params &p, hipStream_t s) {
+  if (p.Sk == 0) return hipSuccess;
+  dim3 gk((p.Sk + RowSplit<D>::ROWS - 1) / RowSplit<D>::ROWS, p.B * p.H);
+  hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, gk, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_rowwise(const Params &p, int dtype, hipStream_t s, void (*f32)(Params),
-                          void (*f16)(Params), void (*bf16)(Params)) {
+template <int D>
+hipError_t bwd_q_f32_d(const Params &p, hipStream_t s) {
+  dim3 gq((p.Sq + RowSplit<D>::ROWS - 1) / RowSplit<D>::ROWS, p.B * p.H);
+  hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, gq, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prep_t(const Params &p, hipStream_t s) {
   const int rows_per_block = 256 / (p.D / 8);
   dim3 grid((p.Sq + rows_per_block - 1) / rows_per_block, p.B * p.H);
-  void (*k)(Params) = dtype == FA_F32 ? f32 : dtype == FA_F16 ? f16 : bf16;
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_prep_kernel<T>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -301,23 +287,28 @@ hipError_t launch_fwd_f32(const Params &p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_f32(const Params &p, hipStream_t s) {
+hipError_t launch_bwd_kv_f32(const Params &p, hipStream_t s) {
   switch (p.D) {
-    case 32: return bwd_f32_d<32>(p, s);
-    case 64: return bwd_f32_d<64>(p, s);
-    case 128: return bwd_f32_d<128>(p, s);
+    case 32: return bwd_kv_f32_d<32>(p, s);
+    case 64: return bwd_kv_f32_d<64>(p, s);
+    case 128: return bwd_kv_f32_d<128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_q_f32(const Params &p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return bwd_q_f32_d<32>(p, s);
+    case 64: return bwd_q_f32_d<64>(p, s);
+    case 128: return bwd_q_f32_d<128>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_prep(const Params &p, int dtype, hipStream_t s) {
-  return launch_rowwise(p, dtype, s, bwd_prep_kernel<float>,
-                                         bwd_prep_kernel<_Float16>, bwd_prep_kernel<__bf16>);
-}
-
-hipError_t launch_bwd_post(const Params &p, int dtype, hipStream_t s) {
-  return launch_rowwise(p, dtype, s, bwd_post_kernel<float>,
-                                         bwd_post_kernel<_Float16>, bwd_post_kernel<__bf16>);
+  if (dtype == FA_F32) return launch_prep_t<float>(p, s);
+  if (dtype == FA_F16) return launch_prep_t<_Float16>(p, s);
+  return launch_prep_t<__bf16>(p, s);
 }
 
 }  // namespace fa

@@ -22,21 +22,22 @@
 // therefore need a single cross-lane exchange per tile, and the running
 // statistics and the O rescale are per-lane scalars.  The P^T operand of
 // the second product is the first product's accumulators rounded to 16 bits
-// in place; V is stored transposed in LDS with the key order inside every
-// 16-key chunk permuted (bits 2 and 3 of the key index swapped) so that each
-// lane's 8 keys sit contiguous and one ds_read_b128 feeds one MFMA operand.
+// in place; the V^T operand comes from the row-major V tile through gfx950's
+// transposing LDS read, in the key order those accumulators hold.
 //
 // Softmax runs in the base-2 domain: t = s * scale * log2(e) + bias * log2(e),
 // p = exp2(t - m); LSE = ln(2) * (m + log2(l)).
 //
-// K/V tiles are double-buffered in LDS: the global loads of tile n+1 are in
-// flight (in VGPRs) while tile n is multiplied; one barrier per tile.
+// K/V tiles are double-buffered in LDS: tile n+1 is loaded from global memory
+// straight into LDS (no register staging) while tile n is multiplied; one
+// barrier per tile.  Tiles use the swizzled layout of fa_tile.h.
 //
 // Tiles with nothing visible are not visited: the causal rule bounds the
 // tile range, key padding bounds it by the first/last valid key of the
 // sample, and a wave whose 32 rows see none of a tile's keys skips its
 // MFMAs.  Per-element mask work happens only on tiles that need it.
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -45,52 +46,19 @@ constexpr int BN = 64;          // keys per tile
 constexpr int kMaxTiles = 512;  // key-tile summaries kept in LDS (S_k <= 32768)
 constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
 
-template <typename T> struct Mfma;
-template <> struct Mfma<__bf16> {
-  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-};
-template <> struct Mfma<_Float16> {
-  static __device__ __forceinline__ f32x16 mac(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-};
-
-// Position of key (or query) `u` (0..15) inside its 16-wide chunk in a
-// transposed LDS tile: bits 2 and 3 swapped.
-__device__ __forceinline__ int chunk_pos(int u) {
-  return (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
-}
-
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
 template <typename T, int D, int NW>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * NW;
   static constexpr int KS = D / 16;        // k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
-  static constexpr int KP = D + 8;         // K tile pitch (elements)
-  static constexpr int VP = BN + 8;        // V^T tile pitch (elements)
-  static constexpr int KCH = BN * D / 8;   // 16-byte chunks of a K tile
-  static constexpr int KCH_T = (KCH + NT - 1) / NT;
-  static constexpr int VU = (BN / 4) * (D / 8);  // 4-row x 8-col units of a V tile
-  static constexpr int VU_T = (VU + NT - 1) / NT;
 };
 
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qtiles) {
   using C = FwdCfg<T, D, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * C::VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
   __shared__ int kv_range[2];
   __shared__ uint32_t tsum[kMaxTiles];  // per key tile: bits 0-7 modality set of valid keys,
                                         // bit 8 some key invalid or past S_k
@@ -193,64 +161,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- global -> register prefetch of one K/V tile
-  u32x4 kreg[C::KCH_T];
-  u32x4 vreg[C::VU_T][4];
-  // rows past S_k read as zeros through the buffer range check
-  auto gload = [&](int kt) {
+  // ---- K and V tiles straight into LDS; rows past S_k read as zeros
+  auto gload = [&](int kt, int buf) {
     const uint32_t base = (uint32_t)kt * BN * krow_b;
-#pragma unroll
-    for (int it = 0; it < C::KCH_T; ++it) {
-      const int c = tid + it * C::NT;
-      const int row = c / (D / 8), col8 = c % (D / 8);
-      if (C::KCH % C::NT == 0 || c < C::KCH)
-        kreg[it] = buf_load16(Kr, base + row * krow_b + col8 * 16);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VU_T; ++it) {
-      const int u = tid + it * C::NT;
-      const int j4 = u % (BN / 4), col8 = u / (BN / 4);
-      if (C::VU % C::NT == 0 || u < C::VU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[it][r] = buf_load16(Vr, base + (4 * j4 + r) * krow_b + col8 * 16);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < C::KCH_T; ++it) {
-      const int c = tid + it * C::NT;
-      const int row = c / (D / 8), col8 = c % (D / 8);
-      if (c < C::KCH) *(u32x4 *)(&Ks[buf][row * C::KP + col8 * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VU_T; ++it) {
-      const int u = tid + it * C::NT;
-      if (u >= C::VU) continue;
-      const int j4 = u % (BN / 4), col8 = u / (BN / 4);
-      const int pos = 16 * (j4 >> 2) + chunk_pos(4 * (j4 & 3));
-      uint16_t *dst = &Vt[buf][(col8 * 8) * C::VP + pos];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t a0 = vreg[it][0][e2], a1 = vreg[it][1][e2];
-        const uint32_t a2 = vreg[it][2][e2], a3 = vreg[it][3][e2];
-        *(u32x2 *)(dst + (2 * e2) * C::VP) = u32x2{lo_halves(a0, a1), lo_halves(a2, a3)};
-        *(u32x2 *)(dst + (2 * e2 + 1) * C::VP) = u32x2{hi_halves(a0, a1), hi_halves(a2, a3)};
-      }
-    }
+    tile_load_lds<D, BN, NW>(Ks[buf], Kr, base, krow_b, w, l);
+    tile_load_lds<D, BN, NW>(Vs[buf], Vr, base, krow_b, w, l);
   };
 
-  if (kt_begin < kt_end) {
-    gload(kt_begin);
-    sstore(0);
-  }
-  __syncthreads();
+  if (kt_begin < kt_end) gload(kt_begin, 0);
+  vm_wait_barrier();
 
   int cur = 0;
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const bool has_next = kt + 1 < kt_end;
-    if (has_next) gload(kt + 1);
+    if (has_next) gload(kt + 1, cur ^ 1);
     const int k0 = kt * BN;
 
     // ---- wave-level tile class: skip, fast (no per-element work) or general
@@ -283,15 +207,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 
     if (!skip) {
       const uint16_t *ks = Ks[cur];
-      const uint16_t *vt = Vt[cur];
+      const uint16_t *vs = Vs[cur];
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int t = 0; t < C::KS; ++t) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const u32x4 a = *(const u32x4 *)(ks + (32 * jb + lr) * C::KP + 16 * t + 8 * g);
-          s[jb] = Mfma<T>::mac(a, qf[t], s[jb]);
+          s[jb] = Mfma<T>::mac(read_row<D>(ks, 32 * jb + lr, 2 * t + g), qf[t], s[jb]);
         }
       }
       // Logit of element r of block jb is  t = cs * s + lane_off  (base-2 units).
@@ -363,21 +286,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
       // O^T += V^T . P^T over four 16-key chunks
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c) {
-        const int jb = c >> 1, r0 = 8 * (c & 1);
-        u32x4 pk;
-        pk[0] = pack2<T>(s[jb][r0 + 0], s[jb][r0 + 1]);
-        pk[1] = pack2<T>(s[jb][r0 + 2], s[jb][r0 + 3]);
-        pk[2] = pack2<T>(s[jb][r0 + 4], s[jb][r0 + 5]);
-        pk[3] = pack2<T>(s[jb][r0 + 6], s[jb][r0 + 7]);
+        const u32x4 pk = pack8<T>(s[c >> 1], 8 * (c & 1));
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const u32x4 a = *(const u32x4 *)(vt + (32 * db + lr) * C::VP + 16 * c + 8 * g);
-          acc[db] = Mfma<T>::mac(a, pk, acc[db]);
-        }
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = Mfma<T>::mac(read_tr<D>(vs, 0, c, 32 * db, l), pk, acc[db]);
       }
     }
-    if (has_next) sstore(cur ^ 1);
-    lds_barrier();
+    vm_wait_barrier();
     cur ^= 1;
   }
 

@@ -14,12 +14,13 @@ hipError_t launch_fwd_mfma(const Params &p, int dtype, hipStream_t s);
 // Forward, fp32 path (D = 32, 64 or 128): fp32 FMA throughout.
 hipError_t launch_fwd_f32(const Params &p, hipStream_t s);
 
-// Backward step 1 (any dtype): delta_i = sum_d dO_id O_id, zero dq_acc.
+// Backward step 1 (any dtype): delta_i = sum_d dO_id O_id.
 hipError_t launch_bwd_prep(const Params &p, int dtype, hipStream_t s);
-// Backward step 2: dK, dV and the float32 dQ accumulator.
-hipError_t launch_bwd_mfma(const Params &p, int dtype, hipStream_t s);
-hipError_t launch_bwd_f32(const Params &p, hipStream_t s);
-// Backward step 3 (any dtype): dQ = scale * dq_acc in dtype/layout.
-hipError_t launch_bwd_post(const Params &p, int dtype, hipStream_t s);
+// Backward step 2: dK, dV (key-tile pass).
+hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_bwd_kv_f32(const Params &p, hipStream_t s);
+// Backward step 3: dQ (query-tile pass), written in dtype/layout.
+hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_bwd_q_f32(const Params &p, hipStream_t s);
 
 }  // namespace fa
