@@ -102,10 +102,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   // staging: Q and dO tiles go straight to LDS (rows past S_q read as zeros);
   // LSE and delta of the block pass through 32 lanes' registers.
   float st_lse = 0.f, st_dlt = 0.f;
+  uint32_t voff[TileGeom<D, QB, NWB>::PER_WAVE];
+  tile_offsets<D, QB, NWB>(voff, qrow_b, w, l);
   auto gload = [&](int it, int buf) {
     const uint32_t base = (uint32_t)it * QB * qrow_b;
-    tile_load_lds<D, QB, NWB>(Qs[buf], Qr, base, qrow_b, w, l);
-    tile_load_lds<D, QB, NWB>(Gs[buf], Gr, base, qrow_b, w, l);
+    tile_load<D, QB, NWB>(Qs[buf], Qr, voff, base, w);
+    tile_load<D, QB, NWB>(Gs[buf], Gr, voff, base, w);
     if (tid < QB) {
       const int i = it * QB + tid;
       const float v = i < p.Sq ? p.lse[rbase + i] : -INFINITY;
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 // ===========================================================================
 // query pass: dQ
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void bwd_q_kernel(Params p, int n_qtiles) {
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBQ * D];
@@ -283,10 +285,12 @@ __global__ __launch_bounds__(256, 1) void bwd_q_kernel(Params p, int n_qtiles) {
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   // K and V tiles go straight to LDS; rows past S_k read as zeros
+  uint32_t voff[TileGeom<D, KBQ, NWB>::PER_WAVE];
+  tile_offsets<D, KBQ, NWB>(voff, krow_b, w, l);
   auto gload = [&](int kt, int buf) {
     const uint32_t base = (uint32_t)kt * KBQ * krow_b;
-    tile_load_lds<D, KBQ, NWB>(Ks[buf], Kr, base, krow_b, w, l);
-    tile_load_lds<D, KBQ, NWB>(Vs[buf], Vr, base, krow_b, w, l);
+    tile_load<D, KBQ, NWB>(Ks[buf], Kr, voff, base, w);
+    tile_load<D, KBQ, NWB>(Vs[buf], Vr, voff, base, w);
   };
 
   if (kt_end > 0) gload(0, 0);

@@ -161,20 +161,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- K and V tiles straight into LDS; rows past S_k read as zeros
+  // ---- K and V tiles straight into LDS; rows past S_k read as zeros.
+  // Key tiles are walked from the last one down: under ALiBi the largest
+  // logits (the keys nearest the diagonal) come first, so the running max
+  // settles early and the lazy rescale below rarely fires.
+  uint32_t voff[TileGeom<D, BN, NW>::PER_WAVE];
+  tile_offsets<D, BN, NW>(voff, krow_b, w, l);
   auto gload = [&](int kt, int buf) {
     const uint32_t base = (uint32_t)kt * BN * krow_b;
-    tile_load_lds<D, BN, NW>(Ks[buf], Kr, base, krow_b, w, l);
-    tile_load_lds<D, BN, NW>(Vs[buf], Vr, base, krow_b, w, l);
+    tile_load<D, BN, NW>(Ks[buf], Kr, voff, base, w);
+    tile_load<D, BN, NW>(Vs[buf], Vr, voff, base, w);
   };
 
-  if (kt_begin < kt_end) gload(kt_begin, 0);
+  if (kt_begin < kt_end) gload(kt_end - 1, 0);
   vm_wait_barrier();
 
   int cur = 0;
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) gload(kt + 1, cur ^ 1);
+  for (int kt = kt_end - 1; kt >= kt_begin; --kt) {
+    const bool has_next = kt > kt_begin;
+    if (has_next) gload(kt - 1, cur ^ 1);
     const int k0 = kt * BN;
 
     // ---- wave-level tile class: skip, fast (no per-element work) or general

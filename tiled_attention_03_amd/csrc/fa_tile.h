@@ -83,27 +83,45 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, int r0, int c, in
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
-// Direct global -> LDS load of rows [0, R) of a D-wide tile whose row 0 is
-// the buffer row at byte offset `gbase` (row stride `rowb` bytes); rows past
-// the buffer's end read as zeros.  Each wave instruction fills 1 KB of LDS
-// (lane l writes bytes [16l, 16l + 16) after the base the instruction names),
-// i.e. 512/D consecutive rows; lane l fetches the logical chunk that the
-// swizzle puts at its physical position.  The loads are asynchronous: wait
-// for vmcnt before the tile is read (vm_wait_barrier).
+// Direct global -> LDS loads of a tile of R rows of D 16-bit elements.  Each
+// wave instruction fills 1 KB of LDS (lane l writes bytes [16l, 16l + 16)
+// after the base the instruction names), i.e. 512/D consecutive rows, and
+// lane l fetches the logical chunk that the swizzle puts at its physical
+// position.  The per-lane byte offsets do not depend on the tile, so they are
+// computed once (tile_offsets); a tile is then named by a uniform byte offset
+// (the buffer's soffset).  Rows past the buffer's end read as zeros.  The
+// loads are asynchronous: wait for vmcnt before the tile is read.
 template <int D, int R, int NW>
-__device__ __forceinline__ void tile_load_lds(uint16_t *tile, __amdgpu_buffer_rsrc_t rs,
-                                              uint32_t gbase, uint32_t rowb, int w, int l) {
-  constexpr int RPI = 512 / D;   // rows per wave instruction
-  constexpr int NI = R / RPI;    // wave instructions per tile
+struct TileGeom {
+  static constexpr int RPI = 512 / D;   // rows per wave instruction
+  static constexpr int NI = R / RPI;    // wave instructions per tile
+  static constexpr int PER_WAVE = NI / NW;
   static_assert(NI % NW == 0, "tile must split evenly over the waves");
+};
+
+// Per-lane byte offsets of this wave's share of a tile (computed once).
+template <int D, int R, int NW>
+__device__ __forceinline__ void tile_offsets(uint32_t *voff, uint32_t rowb, int w, int l) {
+  using G = TileGeom<D, R, NW>;
   const int rsub = l / (D / 8), pc = l % (D / 8);
 #pragma unroll
-  for (int k = 0; k < NI / NW; ++k) {
-    const int r0 = (k * NW + w) * RPI;
-    const int row = r0 + rsub;
-    const uint32_t off = gbase + (uint32_t)row * rowb + (uint32_t)((pc ^ swz<D>(row)) << 4);
+  for (int k = 0; k < G::PER_WAVE; ++k) {
+    const int row = (k * NW + w) * G::RPI + rsub;
+    voff[k] = (uint32_t)row * rowb + (uint32_t)((pc ^ swz<D>(row)) << 4);
+  }
+}
+
+// Issues this wave's loads of the tile whose row 0 sits at byte `tile_base`.
+template <int D, int R, int NW>
+__device__ __forceinline__ void tile_load(uint16_t *tile, __amdgpu_buffer_rsrc_t rs,
+                                          const uint32_t *voff, uint32_t tile_base, int w) {
+  using G = TileGeom<D, R, NW>;
+#pragma unroll
+  for (int k = 0; k < G::PER_WAVE; ++k) {
+    const int r0 = (k * NW + w) * G::RPI;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void *)(tile + r0 * D), 16, off, 0, 0, 0);
+        rs, (__attribute__((address_space(3))) void *)(tile + r0 * D), 16, voff[k],
+        (int)tile_base, 0, 0);
   }
 }
 
