@@ -25,11 +25,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
-KERNEL_SOURCES = {
-    "fwd": "tiled_attention_03_amd/csrc/fa_fwd.hip",
-    "bwd_main": "tiled_attention_03_amd/csrc/fa_bwd.hip",
-    "bwd_post": "tiled_attention_03_amd/csrc/fa_bwd.hip",
+_CSRC = "tiled_attention_03_amd/csrc/"
+KERNEL_SOURCES = {   # files whose text decides each timed kernel's code
+    "fwd": [_CSRC + f for f in ("fa_fwd.hip", "fa_tile.h", "fa_common.h")],
+    "bwd_main": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
+    "bwd_post": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
 }
+# Algorithmic flops per visible (query, key) pair, in units of D, per timed call:
+# forward Q K^T and P V; the key pass (bwd_main) recomputes Q K^T and forms
+# dO V^T, P^T dO and dS^T Q; the query pass (bwd_post) adds dS K (its own
+# recompute of Q K^T and dO V^T is extra work, not counted).
+FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_prep": 0, "bwd_main": 8, "bwd_post": 2}
 
 
 def visible_pairs(pr) -> int:
@@ -64,9 +70,12 @@ def visible_pairs(pr) -> int:
     return total
 
 
-def source_sha(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str):
@@ -191,8 +200,8 @@ def main():
     fwd_tf = f_fwd / (per["fwd"] * 1e-3) / 1e12
     bwd_ms = per["bwd_prep"] + per["bwd_main"] + per["bwd_post"]
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
-    dom = max(("fwd", "bwd_main"), key=lambda n: per[n])
-    dom_flops = f_fwd if dom == "fwd" else f_bwd
+    dom = max(("fwd", "bwd_main", "bwd_post"), key=lambda n: per[n])
+    dom_flops = FLOPS_PER_PAIR_D[dom] * D * pairs
     achieved = dom_flops / (per[dom] * 1e-3) / 1e12
     traffic = traffic_for(dom)
     dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[pr.dtype]
@@ -222,7 +231,10 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": dom_flops},
+        "kernel_tflops": {n: round(FLOPS_PER_PAIR_D[n] * D * pairs / (per[n] * 1e-3) / 1e12, 2)
+                          for n in names if FLOPS_PER_PAIR_D[n]},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pr, heads=args.cpu_heads) if args.config == 5 else None
