@@ -146,10 +146,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
       const uint16_t *qs = Qs[cur];
       const uint16_t *gs = Gs[cur];
       f32x16 s = f32x16{}, dp = f32x16{};
+      // operand reads are issued in batches ahead of their MFMAs (the
+      // scheduling fence keeps them from being sunk next to each use, which
+      // would expose the LDS latency on every product)
 #pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        s = Mfma<T>::mac(read_row<D>(qs, lr, 2 * t + g), kf[t], s);
-        dp = Mfma<T>::mac(read_row<D>(gs, lr, 2 * t + g), vf[t], dp);
+      for (int t0 = 0; t0 < KS; t0 += 4) {
+        u32x4 qa[4], ga[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          qa[t] = read_row<D>(qs, lr, 2 * (t0 + t) + g);
+          ga[t] = read_row<D>(gs, lr, 2 * (t0 + t) + g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          s = Mfma<T>::mac(qa[t], kf[t0 + t], s);
+          dp = Mfma<T>::mac(ga[t], vf[t0 + t], dp);
+        }
       }
       // element r: query i0 + il, il = 8(r/4) + 4g + r%4; key my_j
       if (!general) {
@@ -194,10 +207,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
       for (int c = 0; c < 2; ++c) {
         const u32x4 pp = pack8<T>(s, 8 * c);
         const u32x4 pd = pack8<T>(dp, 8 * c);
+        u32x4 gt[DB], qt[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = Mfma<T>::mac(pp, read_tr<D>(gs, 0, c, 32 * db, l), dv[db]);
-          dk[db] = Mfma<T>::mac(pd, read_tr<D>(qs, 0, c, 32 * db, l), dk[db]);
+          gt[db] = read_tr<D>(gs, 0, c, 32 * db, l);
+          qt[db] = read_tr<D>(qs, 0, c, 32 * db, l);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = Mfma<T>::mac(pp, gt[db], dv[db]);
+          dk[db] = Mfma<T>::mac(pd, qt[db], dk[db]);
         }
       }
     }
@@ -316,9 +336,19 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
       for (int jb = 0; jb < 2; ++jb) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          s = Mfma<T>::mac(read_row<D>(ks, 32 * jb + lr, 2 * t + g), qf[t], s);
-          dp = Mfma<T>::mac(read_row<D>(vs, 32 * jb + lr, 2 * t + g), gf[t], dp);
+        for (int t0 = 0; t0 < KS; t0 += 4) {
+          u32x4 ka[4], va[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            ka[t] = read_row<D>(ks, 32 * jb + lr, 2 * (t0 + t) + g);
+            va[t] = read_row<D>(vs, 32 * jb + lr, 2 * (t0 + t) + g);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            s = Mfma<T>::mac(ka[t], qf[t0 + t], s);
+            dp = Mfma<T>::mac(va[t], gf[t0 + t], dp);
+          }
         }
         // element r: key k0 + 32jb + 8(r/4) + 4g + r%4, query my_i
         if (!general) {
@@ -349,9 +379,12 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const u32x4 pd = pack8<T>(dp, 8 * hh);
+          u32x4 kt[DB];
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = Mfma<T>::mac(read_tr<D>(ks, 0, 2 * jb + hh, 32 * db, l), pd, acc[db]);
+          for (int db = 0; db < DB; ++db) kt[db] = read_tr<D>(ks, 0, 2 * jb + hh, 32 * db, l);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(kt[db], pd, acc[db]);
         }
       }
     }

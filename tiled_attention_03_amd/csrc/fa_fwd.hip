@@ -215,12 +215,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
       const uint16_t *vs = Vs[cur];
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2] = {f32x16{}, f32x16{}};
+      // operand reads in batches ahead of their MFMAs (the scheduling fence
+      // keeps the LDS latency from being exposed on each product)
 #pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
+      for (int t0 = 0; t0 < C::KS; t0 += 4) {
+        u32x4 ka[4][2];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          s[jb] = Mfma<T>::mac(read_row<D>(ks, 32 * jb + lr, 2 * t + g), qf[t], s[jb]);
-        }
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) ka[t][jb] = read_row<D>(ks, 32 * jb + lr, 2 * (t0 + t) + g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) s[jb] = Mfma<T>::mac(ka[t][jb], qf[t0 + t], s[jb]);
       }
       // Logit of element r of block jb is  t = cs * s + lane_off  (base-2 units).
       // Fast tiles: cs = scale*log2(e), the ALiBi term split into a per-register
@@ -292,9 +300,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c) {
         const u32x4 pk = pack8<T>(s[c >> 1], 8 * (c & 1));
+        u32x4 va[C::DB];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = Mfma<T>::mac(read_tr<D>(vs, 0, c, 32 * db, l), pk, acc[db]);
+        for (int db = 0; db < C::DB; ++db) va[db] = read_tr<D>(vs, 0, c, 32 * db, l);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] = Mfma<T>::mac(va[db], pk, acc[db]);
       }
     }
     vm_wait_barrier();
