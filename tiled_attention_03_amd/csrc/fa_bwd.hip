@@ -49,8 +49,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QB * D], Q1[QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t G0[QB * D], G1[QB * D];
   __shared__ __attribute__((aligned(16))) float lam_s[2][QB];   // LSE*log2e (+ALiBi row term)
   __shared__ __attribute__((aligned(16))) float lse_s[2][QB];   // LSE*log2e
   __shared__ __attribute__((aligned(16))) float dlt_s[2][QB];
@@ -104,10 +104,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   float st_lse = 0.f, st_dlt = 0.f;
   uint32_t voff[TileGeom<D, QB, NWB>::PER_WAVE];
   tile_offsets<D, QB, NWB>(voff, qrow_b, w, l);
-  auto gload = [&](int it, int buf) {
+  auto gload = [&](int it, uint16_t *qdst, uint16_t *gdst) {
     const uint32_t base = (uint32_t)it * QB * qrow_b;
-    tile_load<D, QB, NWB>(Qs[buf], Qr, voff, base, w);
-    tile_load<D, QB, NWB>(Gs[buf], Gr, voff, base, w);
+    tile_load<D, QB, NWB>(qdst, Qr, voff, base, w);
+    tile_load<D, QB, NWB>(gdst, Gr, voff, base, w);
     if (tid < QB) {
       const int i = it * QB + tid;
       const float v = i < p.Sq ? p.lse[rbase + i] : -INFINITY;
@@ -124,15 +124,27 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   };
 
   if (it_begin < it_end) {
-    gload(it_begin, 0);
+    gload(it_begin, Q0, G0);
     sstore(0);
   }
   vm_wait_barrier();
 
-  int cur = 0;
-  for (int it = it_begin; it < it_end; ++it) {
+  // per-lane LDS byte offsets: Q/dO rows (A operands) and their transposed reads
+  uint32_t ro[KS], to[2 * DB];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
+
+  // one query block held in buffer `cur`; the next block goes into the other
+  auto block_step = [&](int it, auto buf) {
+    constexpr int cur = decltype(buf)::value;
+    const uint16_t *qs = cur ? Q1 : Q0;
+    const uint16_t *gs = cur ? G1 : G0;
     const bool has_next = it + 1 < it_end;
-    if (has_next) gload(it + 1, cur ^ 1);
+    if (has_next) gload(it + 1, cur ? Q0 : Q1, cur ? G0 : G1);
+    opaque(ro);
+    opaque(to);
     const int i0 = it * QB;
     // wave-level class of the (32 queries x 32 keys) block: fast (no
     // per-element work) or general.  Blocks the mask hides wholly are rare
@@ -143,8 +155,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     if (causal && jw + 31 > i0) general = true;
     if (alibi && !(i0 >= jw + 31)) general = true;   // fast ALiBi form needs i >= j
     {
-      const uint16_t *qs = Qs[cur];
-      const uint16_t *gs = Gs[cur];
       f32x16 s = f32x16{}, dp = f32x16{};
       // operand reads are issued in batches ahead of their MFMAs (the
       // scheduling fence keeps them from being sunk next to each use, which
@@ -154,8 +164,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
         u32x4 qa[4], ga[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          qa[t] = read_row<D>(qs, lr, 2 * (t0 + t) + g);
-          ga[t] = read_row<D>(gs, lr, 2 * (t0 + t) + g);
+          qa[t] = read_row_at<D>(qs, 0, ro[t0 + t]);
+          ga[t] = read_row_at<D>(gs, 0, ro[t0 + t]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -210,8 +220,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
         u32x4 gt[DB], qt[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          gt[db] = read_tr<D>(gs, 0, c, 32 * db, l);
-          qt[db] = read_tr<D>(qs, 0, c, 32 * db, l);
+          gt[db] = read_tr_at<D>(gs, c, &to[2 * db]);
+          qt[db] = read_tr_at<D>(qs, c, &to[2 * db]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -223,8 +233,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     }
     if (has_next) sstore(cur ^ 1);
     vm_wait_barrier();
-    cur ^= 1;
+  };
+  int it = it_begin;
+  for (; it + 1 < it_end; it += 2) {
+    block_step(it, BufIdx<0>{});
+    block_step(it + 1, BufIdx<1>{});
   }
+  if (it < it_end) block_step(it, BufIdx<0>{});
 
   // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
   T *DKg = (T *)p.dk + koff;
@@ -307,19 +322,29 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   // K and V tiles go straight to LDS; rows past S_k read as zeros
   uint32_t voff[TileGeom<D, KBQ, NWB>::PER_WAVE];
   tile_offsets<D, KBQ, NWB>(voff, krow_b, w, l);
-  auto gload = [&](int kt, int buf) {
+  auto gload = [&](int kt, uint16_t *kdst, uint16_t *vdst) {
     const uint32_t base = (uint32_t)kt * KBQ * krow_b;
-    tile_load<D, KBQ, NWB>(Ks[buf], Kr, voff, base, w);
-    tile_load<D, KBQ, NWB>(Vs[buf], Vr, voff, base, w);
+    tile_load<D, KBQ, NWB>(kdst, Kr, voff, base, w);
+    tile_load<D, KBQ, NWB>(vdst, Vr, voff, base, w);
   };
 
-  if (kt_end > 0) gload(0, 0);
+  if (kt_end > 0) gload(0, Ks[0], Vs[0]);
   vm_wait_barrier();
 
-  int cur = 0;
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) gload(kt + 1, cur ^ 1);
+  // per-lane LDS byte offsets: K/V rows (A operands) and K^T reads
+  uint32_t ro[KS], to[2 * DB];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
+
+  // One key tile per step.  This kernel keeps a runtime buffer index (a
+  // statically unrolled pair of steps needs more registers than it has
+  // here), so its LDS reads also wait for the next tile's loads.
+  for (int kt = 0, cur = 0; kt < kt_end; ++kt, cur ^= 1) {
+    const uint16_t *ks = Ks[cur];
+    const uint16_t *vs = Vs[cur];
+    if (kt + 1 < kt_end) gload(kt + 1, Ks[cur ^ 1], Vs[cur ^ 1]);
     const int k0 = kt * KBQ;
     // fast or general tile; tiles hidden from this wave (at most one per
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
@@ -328,8 +353,6 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
     {
-      const uint16_t *ks = Ks[cur];
-      const uint16_t *vs = Vs[cur];
       const float off = (alibi ? sl2 * (float)(k0 + 4 * g - my_i) : 0.f) - lse2;
       // one 32-key block at a time (LSE is known: no row max to wait for)
 #pragma unroll
@@ -340,8 +363,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
           u32x4 ka[4], va[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            ka[t] = read_row<D>(ks, 32 * jb + lr, 2 * (t0 + t) + g);
-            va[t] = read_row<D>(vs, 32 * jb + lr, 2 * (t0 + t) + g);
+            ka[t] = read_row_at<D>(ks, 32 * jb, ro[t0 + t]);
+            va[t] = read_row_at<D>(vs, 32 * jb, ro[t0 + t]);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -379,17 +402,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const u32x4 pd = pack8<T>(dp, 8 * hh);
-          u32x4 kt[DB];
+          u32x4 kop[DB];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) kt[db] = read_tr<D>(ks, 0, 2 * jb + hh, 32 * db, l);
+          for (int db = 0; db < DB; ++db) kop[db] = read_tr_at<D>(ks, 2 * jb + hh, &to[2 * db]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(kt[db], pd, acc[db]);
+          for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(kop[db], pd, acc[db]);
         }
       }
     }
     vm_wait_barrier();
-    cur ^= 1;
   }
 
   // dQ = scale * acc; element (db, r): column 32db + 8(r/4) + 4g + r%4

@@ -104,7 +104,8 @@ __device__ __forceinline__ uint32_t span_bytes(int rows, int64_t stride, int d, 
 // other wave's LDS writes.  Outstanding global loads, stores and atomics are
 // not waited for (a plain __syncthreads() fence would wait for them too).
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // ------------------------------------------------------------------------

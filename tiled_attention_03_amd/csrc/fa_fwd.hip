@@ -57,8 +57,8 @@ struct FwdCfg {
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qtiles) {
   using C = FwdCfg<T, D, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
   __shared__ int kv_range[2];
   __shared__ uint32_t tsum[kMaxTiles];  // per key tile: bits 0-7 modality set of valid keys,
                                         // bit 8 some key invalid or past S_k
@@ -167,19 +167,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   // settles early and the lazy rescale below rarely fires.
   uint32_t voff[TileGeom<D, BN, NW>::PER_WAVE];
   tile_offsets<D, BN, NW>(voff, krow_b, w, l);
-  auto gload = [&](int kt, int buf) {
+  auto gload = [&](int kt, uint16_t *kdst, uint16_t *vdst) {
     const uint32_t base = (uint32_t)kt * BN * krow_b;
-    tile_load<D, BN, NW>(Ks[buf], Kr, voff, base, w);
-    tile_load<D, BN, NW>(Vs[buf], Vr, voff, base, w);
+    tile_load<D, BN, NW>(kdst, Kr, voff, base, w);
+    tile_load<D, BN, NW>(vdst, Vr, voff, base, w);
   };
 
-  if (kt_begin < kt_end) gload(kt_end - 1, 0);
+  if (kt_begin < kt_end) gload(kt_end - 1, K0, V0);
   vm_wait_barrier();
 
-  int cur = 0;
-  for (int kt = kt_end - 1; kt >= kt_begin; --kt) {
-    const bool has_next = kt > kt_begin;
-    if (has_next) gload(kt - 1, cur ^ 1);
+  // per-lane LDS byte offsets: K rows (A operand of S^T) and V^T reads
+  uint32_t ro[C::KS], to[2 * C::DB];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
+
+  // one key tile held in buffer B; the next tile goes into the other buffer
+  auto tile_step = [&](int kt, auto buf) {
+    constexpr int B = decltype(buf)::value;
+    uint16_t *ks = B ? K1 : K0;
+    uint16_t *vs = B ? V1 : V0;
+    if (kt > kt_begin) gload(kt - 1, B ? K0 : K1, B ? V0 : V1);
+    opaque(ro);
+    opaque(to);
     const int k0 = kt * BN;
 
     // ---- wave-level tile class: skip, fast (no per-element work) or general
@@ -211,8 +222,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     }
 
     if (!skip) {
-      const uint16_t *ks = Ks[cur];
-      const uint16_t *vs = Vs[cur];
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2] = {f32x16{}, f32x16{}};
       // operand reads in batches ahead of their MFMAs (the scheduling fence
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int jb = 0; jb < 2; ++jb) ka[t][jb] = read_row<D>(ks, 32 * jb + lr, 2 * (t0 + t) + g);
+          for (int jb = 0; jb < 2; ++jb) ka[t][jb] = read_row_at<D>(ks, 32 * jb, ro[t0 + t]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -302,15 +311,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
         const u32x4 pk = pack8<T>(s[c >> 1], 8 * (c & 1));
         u32x4 va[C::DB];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) va[db] = read_tr<D>(vs, 0, c, 32 * db, l);
+        for (int db = 0; db < C::DB; ++db) va[db] = read_tr_at<D>(vs, c, &to[2 * db]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) acc[db] = Mfma<T>::mac(va[db], pk, acc[db]);
       }
     }
     vm_wait_barrier();
-    cur ^= 1;
+  };
+  int kt = kt_end - 1;
+  for (; kt > kt_begin; kt -= 2) {
+    tile_step(kt, BufIdx<0>{});
+    tile_step(kt - 1, BufIdx<1>{});
   }
+  if (kt == kt_begin) tile_step(kt, BufIdx<0>{});
 
   // ---- epilogue: O = acc / l, LSE
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -22,6 +22,8 @@
 // transposed reads below fetch exactly that order.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -83,6 +85,52 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, int r0, int c, in
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// The same two reads from per-lane byte offsets computed once per kernel.
+// With double buffering, each buffer is its own LDS variable (see BufIdx) at a
+// fixed address; passing the offsets through opaque() once per step keeps the
+// compiler from hoisting one full set of addresses per buffer out of the
+// loop: the buffer's address then folds into the instruction's immediate
+// offset, and one set of offset registers serves both buffers.
+template <int D>
+__device__ __forceinline__ uint32_t row_off(int r, int c) {
+  return 2u * (uint32_t)chunk_off<D>(r, c);
+}
+
+// 8 elements of row (r + dr) at chunk c, with off = row_off(r, c) and dr a
+// multiple of 16 (which leaves the swizzle unchanged).
+template <int D>
+__device__ __forceinline__ u32x4 read_row_at(const uint16_t *tile, int dr, uint32_t off) {
+  return *(const u32x4 *)((const char *)(tile + dr * D) + off);
+}
+
+// Offsets of the two halves of read_tr(tile, 0, 0, n0, l); chunk c of the
+// contraction is 16c rows further down (same swizzle).
+template <int D>
+__device__ __forceinline__ void tr_off(uint32_t o[2], int n0, int l) {
+  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int row = 4 * (l >> 5) + ((l & 15) >> 2);
+  const int cc = col >> 3, within = col & 7;
+  o[0] = 2u * (uint32_t)(row * D + ((cc ^ swz<D>(row)) << 3) + within);
+  o[1] = 2u * (uint32_t)((row + 8) * D + ((cc ^ swz<D>(row + 8)) << 3) + within);
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 read_tr_at(const uint16_t *tile, int c, const uint32_t o[2]) {
+  const char *base = (const char *)(tile + 16 * c * D);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + o[0]));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + o[1]));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Makes the values look modified (they are not) so that nothing computed from
+// them is hoisted out of the enclosing loop.
+template <int N>
+__device__ __forceinline__ void opaque(uint32_t (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
 // Direct global -> LDS loads of a tile of R rows of D 16-bit elements.  Each
 // wave instruction fills 1 KB of LDS (lane l writes bytes [16l, 16l + 16)
 // after the base the instruction names), i.e. 512/D consecutive rows, and
@@ -126,10 +174,22 @@ __device__ __forceinline__ void tile_load(uint16_t *tile, __amdgpu_buffer_rsrc_t
 }
 
 // Waits for this wave's outstanding global loads (including loads into LDS)
-// and LDS operations, then joins the workgroup barrier.
+// and LDS operations, then joins the workgroup barrier.  The wait is the
+// builtin, not inline asm, so that the compiler's own counter bookkeeping
+// knows the loads have retired and adds no waits of its own after it; the
+// barrier's memory clobber keeps LDS accesses on their side of it.
 __device__ __forceinline__ void vm_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);    // no work of either side moves across
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
+
+// Compile-time buffer index of a double-buffered tile.  Each buffer is its own
+// LDS variable and every access names it statically: the compiler can then
+// tell a read of the current buffer from a pending direct-to-LDS load into the
+// other one, and does not make the read wait for that load.
+template <int B> using BufIdx = std::integral_constant<int, B>;
 
 // Rounds 8 accumulator registers r0..r0+7 to 16 bits: the operand slots of
 // one 16-row chunk in the order read_tr uses.
