@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   const int b = bh / p.H, h = bh % p.H;
   const int j0 = kt * KB;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int l = tid & 63, g = l >> 5, lr = l & 31;
   const int jw = j0 + 32 * w;
   const int my_j = jw + lr;
   const uint32_t flags = p.mask_flags;
@@ -273,7 +274,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   const int b = bh / p.H, h = bh % p.H;
   const int q0 = qt * QBQ;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, lr = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int l = tid & 63, g = l >> 5, lr = l & 31;
   const int qw = q0 + 32 * w;
   const int my_i = qw + lr;
   const uint32_t flags = p.mask_flags;
