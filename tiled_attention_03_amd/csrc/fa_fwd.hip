@@ -7,10 +7,12 @@
 // softmax" of its section 1 and of the NPU FlashAttention study's flow
 // description).
 //
-// Workgroup = NW waves, two workgroups per CU (two waves per SIMD).  Each
-// wave owns 32 query rows; the workgroup's BM = 32*NW rows share one stream
-// of K/V tiles of BN = 64 keys.  The products are arranged so that a lane
-// owns ONE query row for the whole kernel:
+// Workgroup = NW waves, one wave per SIMD (each wave has the whole register
+// file).  A wave owns RB = 2 blocks of 32 query rows, so every K or V operand
+// read from LDS feeds two MFMAs (LDS read traffic per flop is what bounds a
+// one-operand-from-LDS design); the workgroup's BM = 32*RB*NW rows share one
+// stream of K/V tiles of BN = 64 keys.  The products are arranged so that a
+// lane owns one query row of each block for the whole kernel:
 //
 //   S^T (keys x queries) = K . Q^T     v_mfma_f32_32x32x16, A = K from LDS,
 //                                      B = Q^T kept in registers
@@ -58,14 +60,18 @@
 namespace fa {
 namespace {
 
-constexpr int BN = 64;          // keys per tile
-constexpr int kMaxTiles = 512;  // key tiles summarised in LDS (S_k <= 32768)
+constexpr int kMaxTiles = 1024;  // key tiles summarised in LDS (S_k <= 32 * kMaxTiles)
 constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int RB_, int KBN_>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
-  static constexpr int BM = 32 * NW;       // query rows per workgroup
+  static constexpr int KBN = KBN_;         // 32-key blocks per tile
+  static constexpr int BN = 32 * KBN;      // keys per tile
+  static constexpr int RB = RB_;           // 32-row blocks per wave
+  static constexpr int WR = 32 * RB;       // query rows per wave
+  static constexpr int OCC = RB == 1 ? 2 : 1;   // waves per SIMD the registers allow
+  static constexpr int BM = WR * NW;       // query rows per workgroup
   static constexpr int KS = D / 16;        // k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
 };
@@ -73,10 +79,12 @@ struct FwdCfg {
 // Tile class for one wave: what the wave does with the tile's scores.
 enum : int { kFast = 0, kGeneral = 1, kDead = 2 };
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qtiles) {
-  using C = FwdCfg<T, D, NW>;
-  constexpr int KS = C::KS, DB = C::DB;
+template <typename T, int D, int NW, int RB_, int KBN_>
+__global__ __launch_bounds__(NW * 64, (FwdCfg<T, D, NW, RB_, KBN_>::OCC))
+void fwd_mfma_kernel(Params p, int n_qtiles) {
+  using C = FwdCfg<T, D, NW, RB_, KBN_>;
+  constexpr int KS = C::KS, DB = C::DB, RB = C::RB, WR = C::WR, KBN = C::KBN, BN = C::BN;
+  constexpr int NC = BN / 16;   // 16-key chunks of a tile
   __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
   __shared__ int kv_range[2];
@@ -95,8 +103,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int l = tid & 63, g = l >> 5, lr = l & 31;
-  const int qw = q0 + 32 * w;   // first row of this wave
-  const int my_i = qw + lr;
+  const int qw = q0 + WR * w;   // first row of this wave
+  int my_i[RB];                 // this lane's row in each block
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) my_i[rb] = qw + 32 * rb + lr;
   const uint32_t flags = p.mask_flags;
   const bool causal = flags & FA_MASK_CAUSAL;
 
@@ -132,11 +142,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 
   // ---- Q^T fragments (B operand), one row per lane, loaded once (rows past
   // S_q read as zeros)
-  u32x4 qf[KS];
-  {
-    const uint32_t qoff = my_i < p.Sq ? (uint32_t)((int64_t)my_i * p.q_ss * ES) : 0x80000000u;
+  u32x4 qf[RB][KS];
 #pragma unroll
-    for (int t = 0; t < KS; ++t) qf[t] = buf_load16(Qr, qoff + (16 * t + 8 * g) * ES);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = my_i[rb];
+    const uint32_t qoff = i < p.Sq ? (uint32_t)((int64_t)i * p.q_ss * ES) : 0x80000000u;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qf[rb][t] = buf_load16(Qr, qoff + (16 * t + 8 * g) * ES);
   }
 
   const bool alibi = p.pse_kind == FA_PSE_ALIBI;
@@ -156,11 +168,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   if (use_summary) {
     for (int kt = w; kt < n_kt_all; kt += NW) {
       const int j = kt * BN + l;
-      bool valid = j < p.Sk;
+      const bool in_tile = l < BN;   // a tile may be narrower than the wave
+      bool valid = in_tile && j < p.Sk;
       int m = 0;
       if (valid && f_pad) valid = p.key_valid[(int64_t)b * p.Sk + j] != 0;
       if (valid && f_mod) m = p.kmod[(int64_t)b * p.Sk + j];
-      uint32_t bits = __ballot(!valid) ? 0x100u : 0u;
+      uint32_t bits = __ballot(in_tile && !valid) ? 0x100u : 0u;
       if (f_mod) {
         for (int mm = 0; mm < p.num_modalities; ++mm)
           if (__ballot(valid && m == mm)) bits |= 1u << mm;
@@ -170,12 +183,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
       if (l == 0) tsum[kt] = bits;
     }
     if (f_mod) {
-      const int mq = my_i < p.Sq ? p.qmod[(int64_t)b * p.Sq + my_i] : -1;
-      for (int mm = 0; mm < p.num_modalities; ++mm) {
-        if (__ballot(mq == mm)) {
-          const uint32_t row = (uint32_t)(p.allow_bits >> (8 * mm)) & 0xffu;
-          allow_any |= row;
-          allow_all &= row;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = my_i[rb];
+        const int mq = i < p.Sq ? p.qmod[(int64_t)b * p.Sq + i] : -1;
+        for (int mm = 0; mm < p.num_modalities; ++mm) {
+          if (__ballot(mq == mm)) {
+            const uint32_t row = (uint32_t)(p.allow_bits >> (8 * mm)) & 0xffu;
+            allow_any |= row;
+            allow_all &= row;
+          }
         }
       }
     }
@@ -227,10 +243,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     return __builtin_amdgcn_readfirstlane((int)tlist[n]);
   };
 
-  f32x16 acc[DB];
+  f32x16 acc[RB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x16{};
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb] = 0.f; }
 
   // ---- tile loads straight into LDS; rows past S_k read as zeros
   uint32_t voff[TileGeom<D, BN, NW>::PER_WAVE];
@@ -247,26 +267,33 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 #pragma unroll
   for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
 
-  // S^T of one tile (two 32-key blocks), operand reads batched ahead of the MFMAs
-  auto scores = [&](const uint16_t *ks, f32x16 (&s)[2]) __attribute__((always_inline)) {
-    s[0] = s[1] = f32x16{};
+  // S^T of one tile (two 32-key blocks) for every row block; operand reads
+  // batched ahead of the MFMAs, each read feeding RB products
+  auto scores = [&](const uint16_t *ks, f32x16 (&s)[RB][KBN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < KBN; ++kb) s[rb][kb] = f32x16{};
 #pragma unroll
     for (int t0 = 0; t0 < KS; t0 += 4) {
-      u32x4 ka[4][2];
+      u32x4 ka[4][KBN];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[t][kb] = read_row_at<D>(ks, 32 * kb, ro[t0 + t]);
+        for (int kb = 0; kb < KBN; ++kb) ka[t][kb] = read_row_at<D>(ks, 32 * kb, ro[t0 + t]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = Mfma<T>::mac(ka[t][kb], qf[t0 + t], s[kb]);
+        for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            s[rb][kb] = Mfma<T>::mac(ka[t][kb], qf[rb][t0 + t], s[rb][kb]);
     }
   };
 
   // O^T += V^T . P^T over the tile's four 16-key chunks
-  auto pv = [&](const uint16_t *vs, const u32x4 (&pk)[4]) __attribute__((always_inline)) {
+  auto pv = [&](const uint16_t *vs, const u32x4 (&pk)[RB][NC]) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
       u32x4 va[DB];
@@ -274,26 +301,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
       for (int db = 0; db < DB; ++db) va[db] = read_tr_at<D>(vs, c, &to[2 * db]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(va[db], pk[c], acc[db]);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][db] = Mfma<T>::mac(va[db], pk[rb][c], acc[rb][db]);
     }
   };
 
-  // lazy rescale: the reference max moves only when the row max mx (already
-  // combined over the lane pair) grows by more than kTau; exp2(t - m_run)
-  // then stays <= 2^kTau and O, l share the same reference.  Returns the
-  // factor that rescales l.
-  auto update_max = [&](float mx) __attribute__((always_inline)) {
-    const bool grow = mx > m_run + kTau;
-    float alpha = 1.f;
-    if (grow) {
-      alpha = exp2_fast(m_run - mx);
-      m_run = mx;
-    }
-    if (__any(grow)) {
+  // lazy rescale: the reference max of a row moves only when its max mx
+  // (already combined over the lane pair) grows by more than kTau;
+  // exp2(t - m_run) then stays <= 2^kTau and O, l share the same reference.
+  // Leaves in alpha the factors that rescale l.
+  auto update_max = [&](const float (&mx)[RB], float (&alpha)[RB]) __attribute__((always_inline)) {
+    bool grow_any = false;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool grow = mx[rb] > m_run[rb] + kTau;
+      alpha[rb] = 1.f;
+      if (grow) {
+        alpha[rb] = exp2_fast(m_run[rb] - mx[rb]);
+        m_run[rb] = mx[rb];
+      }
+      grow_any |= grow;
     }
-    return alpha;
+    if (__any(grow_any)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rb][db] *= alpha[rb];
+    }
   };
 
   // ==== generic phase: one tile per step, per-wave class
@@ -314,20 +349,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     int cls = qw < p.Sq ? kFast : kDead;
     if (dense || f_exp || k0 + BN > p.Sk) cls = max(cls, (int)kGeneral);
     if (causal) {
-      if (k0 > qw + 31) cls = kDead;
+      if (k0 > qw + WR - 1) cls = kDead;
       else if (k0 + BN - 1 > qw) cls = max(cls, (int)kGeneral);
     }
     int adir = 0;   // ALiBi on a tile wholly below (+1) or above (-1) the diagonal
     if (alibi && cls != kDead) {
       if (k0 + BN - 1 <= qw) adir = 1;
-      else if (k0 >= qw + 31) adir = -1;
+      else if (k0 >= qw + WR - 1) adir = -1;
       else cls = kGeneral;
     }
     if (use_summary && cls != kDead) {
       const uint32_t ts = __builtin_amdgcn_readfirstlane(tsum[kt]);
       const uint32_t kset = ts & 0xffu;
       if (f_mod) {
-        const bool diag = p.allow_diag && k0 < qw + 32 && k0 + BN > qw;
+        const bool diag = p.allow_diag && k0 < qw + WR && k0 + BN > qw;
         if ((kset & allow_any) == 0 && !diag) cls = kDead;
         else if ((kset & ~allow_all) != 0 || diag) cls = max(cls, (int)kGeneral);
       } else if (kset == 0) {
@@ -339,62 +374,79 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     }
 
     if (cls != kDead) {
-      f32x16 s[2];
+      f32x16 s[RB][KBN];
       scores(ks, s);
-      // logit of element r of block kb:  t = cs * s + lane_off  (base-2 units)
-      float cs = c_log2, lane_off = 0.f, mx = -INFINITY;
+      // logit of element r of block (rb, kb):  t = cs * s + lane_off[rb]  (base-2 units)
+      float cs = c_log2, lane_off[RB], mx[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) { lane_off[rb] = 0.f; mx[rb] = -INFINITY; }
       if (cls == kFast) {
         if (adir != 0) {
           const float a = adir * sl2c;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s[kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), s[kb][r]);
-          lane_off = adir * sl2 * (float)(k0 + 4 * g - my_i);
+            for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                s[rb][kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), s[rb][kb][r]);
+            lane_off[rb] = adir * sl2 * (float)(k0 + 4 * g - my_i[rb]);
+          }
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaf(mx, cs, lane_off);
+          for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx[rb] = fmaxf(mx[rb], s[rb][kb][r]);
+          mx[rb] = fmaf(mx[rb], cs, lane_off[rb]);
+        }
       } else {
         cs = 1.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = my_i[rb];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            float t = s[kb][r] * c_log2;
-            bool ok = j < p.Sk && my_i < p.Sq;
-            if (ok) ok = allowed_elem(p, b, h, my_i, j);
-            if (ok) {
-              if (alibi) t -= sl2 * fabsf((float)(my_i - j));
-              else if (dense) t += dense_bias(p, b, h, my_i, j) * kLog2e;
-            } else {
-              t = -INFINITY;
+          for (int kb = 0; kb < KBN; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+              float t = s[rb][kb][r] * c_log2;
+              bool ok = j < p.Sk && i < p.Sq;
+              if (ok) ok = allowed_elem(p, b, h, i, j);
+              if (ok) {
+                if (alibi) t -= sl2 * fabsf((float)(i - j));
+                else if (dense) t += dense_bias(p, b, h, i, j) * kLog2e;
+              } else {
+                t = -INFINITY;
+              }
+              s[rb][kb][r] = t;
+              mx[rb] = fmaxf(mx[rb], t);
             }
-            s[kb][r] = t;
-            mx = fmaxf(mx, t);
           }
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float alpha = update_max(mx);
-      const float off = lane_off - (m_run == -INFINITY ? 0.f : m_run);
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int rb = 0; rb < RB; ++rb) mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, 64));
+      float alpha[RB];
+      update_max(mx, alpha);
+      u32x4 pk[RB][NC];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = exp2_fast(fmaf(s[kb][r], cs, off));
-          s[kb][r] = x;
-          part[r & 3] += x;
-        }
-      l_run = l_run * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
-      u32x4 pk[4];
+      for (int rb = 0; rb < RB; ++rb) {
+        const float off = lane_off[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pk[c] = pack8<T>(s[c >> 1], 8 * (c & 1));
+        for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = exp2_fast(fmaf(s[rb][kb][r], cs, off));
+            s[rb][kb][r] = x;
+            part[r & 3] += x;
+          }
+        l_run[rb] = l_run[rb] * alpha[rb] + ((part[0] + part[1]) + (part[2] + part[3]));
+#pragma unroll
+        for (int c = 0; c < NC; ++c) pk[rb][c] = pack8<T>(s[rb][c >> 1], 8 * (c & 1));
+      }
       pv(vs, pk);
     }
     vm_wait_barrier();
@@ -418,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   // ==== fast phase: software pipeline over list entries n_gen .. n_all-1
   const int n_fast = n_all - n_gen;
   auto ftile = [&](int n) __attribute__((always_inline)) { return tile_at(n_gen + n); };
-  f32x16 sA[2], sB[2];
+  f32x16 sA[RB][KBN], sB[RB][KBN];
   if (n_fast > 0) {
     const int f0 = ftile(0);
     load_tile(f0, K0, Kr);
@@ -431,7 +483,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
 
   // one step: softmax of tile n (scores in s), scores of tile n+1 (into sn),
   // O += P V of tile n.  Buffer parity B: K_{n+1} in K[1-B], V_n in V[B].
-  auto fast_step = [&](int n, auto buf, f32x16 (&s)[2], f32x16 (&sn)[2])
+  auto fast_step = [&](int n, auto buf, f32x16 (&s)[RB][KBN], f32x16 (&sn)[RB][KBN])
                        __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     const uint16_t *kn = B ? K0 : K1;   // K of tile n+1
@@ -447,77 +499,99 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
     // into s (coefficient 0 without ALiBi: no branch, the scores stay in place)
     const int adir = k0 + BN - 1 <= q0 ? 1 : -1;
     const float a = alibi ? adir * sl2c : 0.f;
-    const float lane_off = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i) : 0.f;
-    float mx = -INFINITY;
+    float lane_off[RB], mx[RB], off[RB], alpha[RB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      lane_off[rb] = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i[rb]) : 0.f;
+      mx[rb] = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), s[kb][r]);
-        mx = fmaxf(mx, s[kb][r]);
-      }
-    mx = fmaf(mx, c_log2, lane_off);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float alpha = update_max(mx);
-    const float off = lane_off - (m_run == -INFINITY ? 0.f : m_run);
+      for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[rb][kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), s[rb][kb][r]);
+          mx[rb] = fmaxf(mx[rb], s[rb][kb][r]);
+        }
+      mx[rb] = fmaf(mx[rb], c_log2, lane_off[rb]);
+      mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, 64));
+    }
+    update_max(mx, alpha);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) off[rb] = lane_off[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
 
     // Scores of tile n+1 interleaved with the exponentials of tile n, in an
     // order fixed by scheduling fences (only scalar work may cross them): the
     // first half of the K operand reads up front and the rest one k-step
-    // before they are needed,
-    // then per k-step the two score products followed by a share of the
-    // exponentials (which do not depend on them), so the matrix core and the
-    // VALU work side by side.  The V^T reads of the first 16-key chunk go out
-    // three quarters in, those of chunk c+1 ahead of the products of chunk c.
-    // On the last step the scores come from a stale buffer and are unused.
-    constexpr int NE = 32;               // score elements per lane
+    // before they are needed, then per k-step the score products followed by
+    // a share of the exponentials (which do not depend on them), so the
+    // matrix core and the VALU work side by side.  The V^T reads of the first
+    // 16-key chunk go out three quarters in, those of chunk c+1 ahead of the
+    // products of chunk c.  On the last step the scores come from a stale
+    // buffer and are unused.
+    // the matrix-dense part of the step runs at raised issue priority, so the
+    // wave sharing this SIMD fills the gaps with its own VALU work
+    __builtin_amdgcn_s_setprio(1);
+    constexpr int NE = 16 * KBN * RB;    // score elements per lane
     constexpr int EPS = NE / KS;         // exponentials per k-step
-    u32x4 ka[KS][2];
+    u32x4 ka[KS][KBN];
 #pragma unroll
     for (int t = 0; t < KS / 2; ++t)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) ka[t][kb] = read_row_at<D>(kn, 32 * kb, ro[t]);
+      for (int kb = 0; kb < KBN; ++kb) ka[t][kb] = read_row_at<D>(kn, 32 * kb, ro[t]);
     __builtin_amdgcn_sched_barrier(0x0004);
-    sn[0] = sn[1] = f32x16{};
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    u32x4 va[4][DB];
+    float part[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int kb = 0; kb < KBN; ++kb) sn[rb][kb] = f32x16{};
+      part[rb][0] = part[rb][1] = part[rb][2] = part[rb][3] = 0.f;
+    }
+    u32x4 va[NC][DB];
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       if (t == KS / 2 - 1) {
 #pragma unroll
         for (int u = KS / 2; u < KS; ++u)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ka[u][kb] = read_row_at<D>(kn, 32 * kb, ro[u]);
+          for (int kb = 0; kb < KBN; ++kb) ka[u][kb] = read_row_at<D>(kn, 32 * kb, ro[u]);
       }
       if (t == 3 * KS / 4) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) va[0][db] = read_tr_at<D>(vs, 0, &to[2 * db]);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sn[kb] = Mfma<T>::mac(ka[t][kb], qf[t], sn[kb]);
+      for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sn[rb][kb] = Mfma<T>::mac(ka[t][kb], qf[rb][t], sn[rb][kb]);
 #pragma unroll
       for (int e = t * EPS; e < (t + 1) * EPS; ++e) {
-        const int kb = e / 16, r = e % 16;
-        const float x = exp2_fast(fmaf(s[kb][r], c_log2, off));
-        s[kb][r] = x;
-        part[r & 3] += x;   // four short sum chains instead of one long one
+        const int rb = e / (16 * KBN), kb = (e / 16) % KBN, r = e % 16;
+        const float x = exp2_fast(fmaf(s[rb][kb][r], c_log2, off[rb]));
+        s[rb][kb][r] = x;
+        part[rb][r & 3] += x;   // four short sum chains instead of one long one
       }
       __builtin_amdgcn_sched_barrier(0x0004);
     }
-    l_run = l_run * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
-    u32x4 pk[4];
+    u32x4 pk[RB][NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) pk[c] = pack8<T>(s[c >> 1], 8 * (c & 1));
+    for (int rb = 0; rb < RB; ++rb) {
+      l_run[rb] = l_run[rb] * alpha[rb] + ((part[rb][0] + part[rb][1]) + (part[rb][2] + part[rb][3]));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c + 1 < 4) {
+      for (int c = 0; c < NC; ++c) pk[rb][c] = pack8<T>(s[rb][c >> 1], 8 * (c & 1));
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) va[c + 1][db] = read_tr_at<D>(vs, c + 1, &to[2 * db]);
       }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(va[c][db], pk[c], acc[db]);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][db] = Mfma<T>::mac(va[c][db], pk[rb][c], acc[rb][db]);
       __builtin_amdgcn_sched_barrier(0x0004);
     }
+    __builtin_amdgcn_s_setprio(0);
     vm_wait_barrier();
   };
   {
@@ -530,43 +604,52 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(Params p, int n_qt
   }
 
   // ---- epilogue: O = acc / l, LSE
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (my_i < p.Sq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T *Og = (T *)p.o + b * p.q_sb + h * p.q_sh + (int64_t)my_i * p.q_ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = my_i[rb];
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+    if (i < p.Sq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      T *Og = (T *)p.o + b * p.q_sb + h * p.q_sh + (int64_t)i * p.q_ss;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * db + 8 * rr + 4 * g;
-        u32x2 v;
-        v[0] = pack2<T>(acc[db][4 * rr + 0] * inv, acc[db][4 * rr + 1] * inv);
-        v[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
-        *(u32x2 *)(Og + d0) = v;
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = 32 * db + 8 * rr + 4 * g;
+          u32x2 v;
+          v[0] = pack2<T>(acc[rb][db][4 * rr + 0] * inv, acc[rb][db][4 * rr + 1] * inv);
+          v[1] = pack2<T>(acc[rb][db][4 * rr + 2] * inv, acc[rb][db][4 * rr + 3] * inv);
+          *(u32x2 *)(Og + d0) = v;
+        }
       }
+      if (g == 0)
+        p.lse[((int64_t)b * p.H + h) * p.Sq + i] =
+            l_tot > 0.f ? (m_run[rb] + log2f(l_tot)) * kLn2 : -INFINITY;
     }
-    if (g == 0)
-      p.lse[((int64_t)b * p.H + h) * p.Sq + my_i] =
-          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int RB, int KBN>
 hipError_t launch_t(const Params &p, hipStream_t s) {
-  using C = FwdCfg<T, D, NW>;
+  using C = FwdCfg<T, D, NW, RB, KBN>;
   const int n_qtiles = (p.Sq + C::BM - 1) / C::BM;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW>), dim3((unsigned)blocks), dim3(C::NT), 0, s, p,
-                     n_qtiles);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN>), dim3((unsigned)blocks), dim3(C::NT), 0, s,
+                     p, n_qtiles);
   return hipGetLastError();
 }
 
+constexpr int kRB = 1, kKBN = 2;   // tile shape: 32-row blocks per wave, 32-key blocks per tile
+constexpr int kNW = 4;             // waves per workgroup
+
 template <typename T>
 hipError_t launch_dtype(const Params &p, hipStream_t s) {
-  const bool small_q = p.Sq <= 32;
-  if (p.D == 64) return small_q ? launch_t<T, 64, 1>(p, s) : launch_t<T, 64, 4>(p, s);
-  if (p.D == 128) return small_q ? launch_t<T, 128, 1>(p, s) : launch_t<T, 128, 4>(p, s);
+  const bool small_q = p.Sq <= 32 * kRB;
+  if (p.D == 64)
+    return small_q ? launch_t<T, 64, 1, kRB, kKBN>(p, s) : launch_t<T, 64, kNW, kRB, kKBN>(p, s);
+  if (p.D == 128)
+    return small_q ? launch_t<T, 128, 1, kRB, kKBN>(p, s) : launch_t<T, 128, kNW, kRB, kKBN>(p, s);
   return hipErrorInvalidValue;
 }
 
