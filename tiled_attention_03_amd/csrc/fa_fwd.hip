@@ -427,7 +427,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         }
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, 64));
+      for (int rb = 0; rb < RB; ++rb) mx[rb] = max_lane_pair(mx[rb]);
       float alpha[RB];
       update_max(mx, alpha);
       u32x4 pk[RB][NC];
@@ -512,7 +512,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
           mx[rb] = fmaxf(mx[rb], s[rb][kb][r]);
         }
       mx[rb] = fmaf(mx[rb], c_log2, lane_off[rb]);
-      mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32, 64));
+      mx[rb] = max_lane_pair(mx[rb]);
     }
     update_max(mx, alpha);
 #pragma unroll

@@ -123,6 +123,21 @@ __device__ __forceinline__ u32x4 read_tr_at(const uint16_t *tile, int c, const u
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// Max of x over the lane pair (l, l ^ 32), in every lane.  gfx950's
+// v_permlane32_swap exchanges the upper 32 lanes of one register with the
+// lower 32 lanes of another: with both holding x, one ends up with the lower
+// half's values in all 64 lanes and the other with the upper half's, whichever
+// way round; their max is the pair max.  A VALU operation, where a shuffle
+// through ds_bpermute would queue behind the LDS traffic.  (The compiler's
+// builtin for this instruction returns the first result twice, so it is
+// written out; the nops cover the VALU write -> permlane read hazard and its
+// result's first use.)
+__device__ __forceinline__ float max_lane_pair(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 // Makes the values look modified (they are not) so that nothing computed from
 // them is hoisted out of the enclosing loop.
 template <int N>
