@@ -49,11 +49,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[QB * D], Q1[QB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t G0[QB * D], G1[QB * D];
-  __shared__ __attribute__((aligned(16))) float lam_s[2][QB];   // LSE*log2e (+ALiBi row term)
-  __shared__ __attribute__((aligned(16))) float lse_s[2][QB];   // LSE*log2e
-  __shared__ __attribute__((aligned(16))) float dlt_s[2][QB];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QB * D], Q1[QB * D], Q2[QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t G0[QB * D], G1[QB * D], G2[QB * D];
+  __shared__ __attribute__((aligned(16))) float lam_s[3][QB];   // LSE*log2e (+ALiBi row term)
+  __shared__ __attribute__((aligned(16))) float lse_s[3][QB];   // LSE*log2e
+  __shared__ __attribute__((aligned(16))) float dlt_s[3][QB];
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
@@ -124,11 +124,22 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     }
   };
 
-  if (it_begin < it_end) {
-    gload(it_begin, Q0, G0);
-    sstore(0);
+  // Query blocks come in two groups.  Fast blocks need no per-element work
+  // for any key of the workgroup (full blocks, no mask tensors or dense bias,
+  // and under the causal rule or ALiBi every row at or below every key); they
+  // form the range [f0, f1) and run software-pipelined.  The other blocks
+  // (the causal diagonal band, the S_q tail, masked problems) run one block
+  // per step with per-wave classification.  The sums over blocks do not
+  // depend on the order.
+  int f0 = it_end, f1 = it_end;
+  if (!f_elem && !dense && j0 + KB <= p.Sk) {
+    const int first = (causal || alibi) ? max(it_begin, (j0 + KB - 1 + QB - 1) / QB) : it_begin;
+    const int last = p.Sq / QB;   // full blocks only
+    if (first < last) { f0 = first; f1 = last; }
   }
-  vm_wait_barrier();
+  const int n_lead = f0 - it_begin;            // generic blocks before the fast range
+  const int n_gen = n_lead + (it_end - f1);    // and after it
+  auto gen_at = [&](int n) { return n < n_lead ? it_begin + n : f1 + (n - n_lead); };
 
   // per-lane LDS byte offsets: Q/dO rows (A operands) and their transposed reads
   uint32_t ro[KS], to[2 * DB];
@@ -137,29 +148,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 #pragma unroll
   for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
 
-  // one query block held in buffer `cur`; the next block goes into the other
-  auto block_step = [&](int it, auto buf) {
+  // ==== generic blocks: one block per step (buffers 0 and 1)
+  auto gen_step = [&](int n, auto buf) __attribute__((always_inline)) {
     constexpr int cur = decltype(buf)::value;
     const uint16_t *qs = cur ? Q1 : Q0;
     const uint16_t *gs = cur ? G1 : G0;
-    const bool has_next = it + 1 < it_end;
-    if (has_next) gload(it + 1, cur ? Q0 : Q1, cur ? G0 : G1);
+    const bool has_next = n + 1 < n_gen;
+    if (has_next) gload(gen_at(n + 1), cur ? Q0 : Q1, cur ? G0 : G1);
     opaque(ro);
     opaque(to);
-    const int i0 = it * QB;
+    const int i0 = gen_at(n) * QB;
     // wave-level class of the (32 queries x 32 keys) block: fast (no
-    // per-element work) or general.  Blocks the mask hides wholly are rare
-    // here (a few per workgroup) and take the general path, which yields
-    // P = dS = 0; keeping the accumulation unconditional lets the dK/dV
-    // accumulators stay in place across iterations.
+    // per-element work) or general.  Blocks the mask hides wholly take the
+    // general path, which yields P = dS = 0; keeping the accumulation
+    // unconditional lets the dK/dV accumulators stay in place.
     bool general = f_elem || dense || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
     if (causal && jw + 31 > i0) general = true;
     if (alibi && !(i0 >= jw + 31)) general = true;   // fast ALiBi form needs i >= j
     {
       f32x16 s = f32x16{}, dp = f32x16{};
-      // operand reads are issued in batches ahead of their MFMAs (the
-      // scheduling fence keeps them from being sunk next to each use, which
-      // would expose the LDS latency on every product)
+      // operand reads are issued in batches ahead of their MFMAs
 #pragma unroll
       for (int t0 = 0; t0 < KS; t0 += 4) {
         u32x4 qa[4], ga[4];
@@ -235,12 +243,153 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     if (has_next) sstore(cur ^ 1);
     vm_wait_barrier();
   };
-  int it = it_begin;
-  for (; it + 1 < it_end; it += 2) {
-    block_step(it, BufIdx<0>{});
-    block_step(it + 1, BufIdx<1>{});
+
+  if (n_gen > 0) {
+    gload(gen_at(0), Q0, G0);
+    sstore(0);
   }
-  if (it < it_end) block_step(it, BufIdx<0>{});
+  vm_wait_barrier();
+  {
+    int n = 0;
+    for (; n + 1 < n_gen; n += 2) {
+      gen_step(n, BufIdx<0>{});
+      gen_step(n + 1, BufIdx<1>{});
+    }
+    if (n < n_gen) gen_step(n, BufIdx<0>{});
+  }
+
+  // ==== fast blocks: software pipeline over [f0, f1).  Block n sits in
+  // buffer n % 3; step n computes S and dP of block n+1 (A = its Q / dO rows)
+  // interleaved with P and dS of block n (whose scores came from the
+  // previous step), then dV += P^T dO and dK += dS^T Q of block n (transposed
+  // reads of its tiles), while block n+2 loads into the third buffer.
+  const int n_fast = f1 - f0;
+  f32x16 sA = f32x16{}, dpA = f32x16{}, sB = f32x16{}, dpB = f32x16{};
+  // S and dP of the block in buffers (qs, gs), operand reads batched ahead
+  auto scores = [&](const uint16_t *qs, const uint16_t *gs, f32x16 &s, f32x16 &dp)
+                    __attribute__((always_inline)) {
+    s = dp = f32x16{};
+#pragma unroll
+    for (int t0 = 0; t0 < KS; t0 += 4) {
+      u32x4 qa[4], ga[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qa[t] = read_row_at<D>(qs, 0, ro[t0 + t]);
+        ga[t] = read_row_at<D>(gs, 0, ro[t0 + t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s = Mfma<T>::mac(qa[t], kf[t0 + t], s);
+        dp = Mfma<T>::mac(ga[t], vf[t0 + t], dp);
+      }
+    }
+  };
+  if (n_fast > 0) {
+    gload(f0, Q0, G0);
+    sstore(0);
+    if (n_fast > 1) {
+      gload(f0 + 1, Q1, G1);
+      sstore(1);
+    }
+  }
+  vm_wait_barrier();
+  if (n_fast > 0) scores(Q0, G0, sA, dpA);
+
+  auto fast_step = [&](int n, auto buf, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn)
+                       __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value, N1 = (B + 1) % 3, N2 = (B + 2) % 3;
+    const uint16_t *qs = B == 0 ? Q0 : B == 1 ? Q1 : Q2;      // block n
+    const uint16_t *gs = B == 0 ? G0 : B == 1 ? G1 : G2;
+    const uint16_t *qn = N1 == 0 ? Q0 : N1 == 1 ? Q1 : Q2;    // block n+1
+    const uint16_t *gn = N1 == 0 ? G0 : N1 == 1 ? G1 : G2;
+    const bool has_next2 = n + 2 < n_fast;
+    if (has_next2) gload(f0 + n + 2, N2 == 0 ? Q0 : N2 == 1 ? Q1 : Q2, N2 == 0 ? G0 : N2 == 1 ? G1 : G2);
+    opaque(ro);
+    opaque(to);
+    const int i0 = (f0 + n) * QB;
+    const float L = sl2 * (float)(my_j - i0);
+    f32x4 lam[4], dl[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      lam[rr] = *(const f32x4 *)&lam_s[B][8 * rr + 4 * g];
+      dl[rr] = *(const f32x4 *)&dlt_s[B][8 * rr + 4 * g];
+    }
+    // Order fixed by scheduling fences (only scalar work may cross them): the
+    // first half of the next block's operand reads up front, the rest one
+    // k-step before they are needed; per k-step its two score products, then
+    // two elements of this block's P and dS (which do not depend on them);
+    // the transposed reads of this block's first 16-query chunk go out three
+    // quarters in, those of the second ahead of the first chunk's products.
+    // On the last step the next block's scores come from a stale buffer and
+    // are unused.
+    u32x4 qa[KS], ga[KS];
+#pragma unroll
+    for (int t = 0; t < KS / 2; ++t) {
+      qa[t] = read_row_at<D>(qn, 0, ro[t]);
+      ga[t] = read_row_at<D>(gn, 0, ro[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0x0004);
+    sn = dpn = f32x16{};
+    u32x4 gt[2][DB], qt[2][DB];
+    constexpr int EPS = 16 / KS;   // elements of P / dS per k-step
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      if (t == KS / 2 - 1) {
+#pragma unroll
+        for (int u = KS / 2; u < KS; ++u) {
+          qa[u] = read_row_at<D>(qn, 0, ro[u]);
+          ga[u] = read_row_at<D>(gn, 0, ro[u]);
+        }
+      }
+      if (t == 3 * KS / 4) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          gt[0][db] = read_tr_at<D>(gs, 0, &to[2 * db]);
+          qt[0][db] = read_tr_at<D>(qs, 0, &to[2 * db]);
+        }
+      }
+      sn = Mfma<T>::mac(qa[t], kf[t], sn);
+      dpn = Mfma<T>::mac(ga[t], vf[t], dpn);
+#pragma unroll
+      for (int r = t * EPS; r < (t + 1) * EPS; ++r) {
+        const float pr = exp2_fast(fmaf(s[r], c_log2, L - lam[r >> 2][r & 3]));
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - dl[r >> 2][r & 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0x0004);
+    }
+    // dV += P^T dO, dK += dS^T Q over this block's two 16-query chunks
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (c == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          gt[1][db] = read_tr_at<D>(gs, 1, &to[2 * db]);
+          qt[1][db] = read_tr_at<D>(qs, 1, &to[2 * db]);
+        }
+      }
+      const u32x4 pp = pack8<T>(s, 8 * c);
+      const u32x4 pd = pack8<T>(dp, 8 * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = Mfma<T>::mac(pp, gt[c][db], dv[db]);
+        dk[db] = Mfma<T>::mac(pd, qt[c][db], dk[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0x0004);
+    }
+    if (has_next2) sstore(N2);
+    vm_wait_barrier();
+  };
+  // six steps per trip: three buffers times two score register sets
+  for (int n = 0; n < n_fast; n += 6) {
+    fast_step(n, BufIdx<0>{}, sA, dpA, sB, dpB);
+    if (n + 1 < n_fast) fast_step(n + 1, BufIdx<1>{}, sB, dpB, sA, dpA);
+    if (n + 2 < n_fast) fast_step(n + 2, BufIdx<2>{}, sA, dpA, sB, dpB);
+    if (n + 3 < n_fast) fast_step(n + 3, BufIdx<0>{}, sB, dpB, sA, dpA);
+    if (n + 4 < n_fast) fast_step(n + 4, BufIdx<1>{}, sA, dpA, sB, dpB);
+    if (n + 5 < n_fast) fast_step(n + 5, BufIdx<2>{}, sB, dpB, sA, dpA);
+  }
 
   // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
   T *DKg = (T *)p.dk + koff;
