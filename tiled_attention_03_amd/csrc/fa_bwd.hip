@@ -294,9 +294,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     }
   }
   vm_wait_barrier();
+  // row statistics (LSE term, delta) of the block in flight, in registers
+  f32x4 lmA[4], dlA[4], lmB[4], dlB[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    lmA[rr] = *(const f32x4 *)&lam_s[0][8 * rr + 4 * g];
+    dlA[rr] = *(const f32x4 *)&dlt_s[0][8 * rr + 4 * g];
+  }
   if (n_fast > 0) scores(Q0, G0, sA, dpA);
 
-  auto fast_step = [&](int n, auto buf, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn)
+  auto fast_step = [&](int n, auto buf, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn,
+                       f32x4 (&lam)[4], f32x4 (&dl)[4], f32x4 (&lamn)[4], f32x4 (&dln)[4])
                        __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value, N1 = (B + 1) % 3, N2 = (B + 2) % 3;
     const uint16_t *qs = B == 0 ? Q0 : B == 1 ? Q1 : Q2;      // block n
@@ -309,20 +317,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     opaque(to);
     const int i0 = (f0 + n) * QB;
     const float L = sl2 * (float)(my_j - i0);
-    f32x4 lam[4], dl[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      lam[rr] = *(const f32x4 *)&lam_s[B][8 * rr + 4 * g];
-      dl[rr] = *(const f32x4 *)&dlt_s[B][8 * rr + 4 * g];
-    }
     // Order fixed by scheduling fences (only scalar work may cross them): the
     // first half of the next block's operand reads up front, the rest one
     // k-step before they are needed; per k-step its two score products, then
     // two elements of this block's P and dS (which do not depend on them);
-    // the transposed reads of this block's first 16-query chunk go out three
-    // quarters in, those of the second ahead of the first chunk's products.
-    // On the last step the next block's scores come from a stale buffer and
-    // are unused.
+    // the transposed reads of this block's two 16-query chunks go out half
+    // way and three quarters in, and the next block's row statistics during
+    // this block's dV / dK products.  On the last step the next block's
+    // scores and statistics come from stale buffers and are unused.
     u32x4 qa[KS], ga[KS];
 #pragma unroll
     for (int t = 0; t < KS / 2; ++t) {
@@ -342,11 +344,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
           ga[u] = read_row_at<D>(gn, 0, ro[u]);
         }
       }
-      if (t == 3 * KS / 4) {
+      if (t == KS / 2 || t == 3 * KS / 4) {
+        const int c = t == KS / 2 ? 0 : 1;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          gt[0][db] = read_tr_at<D>(gs, 0, &to[2 * db]);
-          qt[0][db] = read_tr_at<D>(qs, 0, &to[2 * db]);
+          gt[c][db] = read_tr_at<D>(gs, c, &to[2 * db]);
+          qt[c][db] = read_tr_at<D>(qs, c, &to[2 * db]);
         }
       }
       sn = Mfma<T>::mac(qa[t], kf[t], sn);
@@ -364,9 +367,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     for (int c = 0; c < 2; ++c) {
       if (c == 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          gt[1][db] = read_tr_at<D>(gs, 1, &to[2 * db]);
-          qt[1][db] = read_tr_at<D>(qs, 1, &to[2 * db]);
+        for (int rr = 0; rr < 4; ++rr) {
+          lamn[rr] = *(const f32x4 *)&lam_s[N1][8 * rr + 4 * g];
+          dln[rr] = *(const f32x4 *)&dlt_s[N1][8 * rr + 4 * g];
         }
       }
       const u32x4 pp = pack8<T>(s, 8 * c);
@@ -381,14 +384,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     if (has_next2) sstore(N2);
     vm_wait_barrier();
   };
-  // six steps per trip: three buffers times two score register sets
+  // six steps per trip: three buffers times two register sets
   for (int n = 0; n < n_fast; n += 6) {
-    fast_step(n, BufIdx<0>{}, sA, dpA, sB, dpB);
-    if (n + 1 < n_fast) fast_step(n + 1, BufIdx<1>{}, sB, dpB, sA, dpA);
-    if (n + 2 < n_fast) fast_step(n + 2, BufIdx<2>{}, sA, dpA, sB, dpB);
-    if (n + 3 < n_fast) fast_step(n + 3, BufIdx<0>{}, sB, dpB, sA, dpA);
-    if (n + 4 < n_fast) fast_step(n + 4, BufIdx<1>{}, sA, dpA, sB, dpB);
-    if (n + 5 < n_fast) fast_step(n + 5, BufIdx<2>{}, sB, dpB, sA, dpA);
+    fast_step(n, BufIdx<0>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
+    if (n + 1 < n_fast) fast_step(n + 1, BufIdx<1>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
+    if (n + 2 < n_fast) fast_step(n + 2, BufIdx<2>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
+    if (n + 3 < n_fast) fast_step(n + 3, BufIdx<0>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
+    if (n + 4 < n_fast) fast_step(n + 4, BufIdx<1>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
+    if (n + 5 < n_fast) fast_step(n + 5, BufIdx<2>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
   }
 
   // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
