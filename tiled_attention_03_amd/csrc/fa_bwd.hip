@@ -321,9 +321,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     // first half of the next block's operand reads up front, the rest one
     // k-step before they are needed; per k-step its two score products, then
     // two elements of this block's P and dS (which do not depend on them);
-    // the transposed reads of this block's two 16-query chunks go out half
-    // way and three quarters in, and the next block's row statistics during
-    // this block's dV / dK products.  On the last step the next block's
+    // the transposed reads of this block's two 16-query chunks go out at the
+    // second k-step and half way, and the next block's row statistics during
+    // this block's last dV / dK products.  On the last step the next block's
     // scores and statistics come from stale buffers and are unused.
     u32x4 qa[KS], ga[KS];
 #pragma unroll
@@ -335,6 +335,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     sn = dpn = f32x16{};
     u32x4 gt[2][DB], qt[2][DB];
     constexpr int EPS = 16 / KS;   // elements of P / dS per k-step
+    constexpr int DBS = 2 * DB / KS;   // chunk-0 d-blocks of dV / dK per late k-step
+    u32x4 pp0, pd0;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       if (t == KS / 2 - 1) {
@@ -344,8 +346,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
           ga[u] = read_row_at<D>(gn, 0, ro[u]);
         }
       }
-      if (t == KS / 2 || t == 3 * KS / 4) {
-        const int c = t == KS / 2 ? 0 : 1;
+      if (t == 1 || t == KS / 2) {
+        const int c = t == 1 ? 0 : 1;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           gt[c][db] = read_tr_at<D>(gs, c, &to[2 * db]);
@@ -354,6 +356,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
       }
       sn = Mfma<T>::mac(qa[t], kf[t], sn);
       dpn = Mfma<T>::mac(ga[t], vf[t], dpn);
+      if (t >= KS / 2) {
+        // chunk 0 (elements 0..7) is complete: its dV / dK products fill the
+        // second half of the k-steps
+        if (t == KS / 2) {
+          pp0 = pack8<T>(s, 0);
+          pd0 = pack8<T>(dp, 0);
+        }
+#pragma unroll
+        for (int db = (t - KS / 2) * DBS; db < (t - KS / 2 + 1) * DBS; ++db) {
+          dv[db] = Mfma<T>::mac(pp0, gt[0][db], dv[db]);
+          dk[db] = Mfma<T>::mac(pd0, qt[0][db], dk[db]);
+        }
+      }
 #pragma unroll
       for (int r = t * EPS; r < (t + 1) * EPS; ++r) {
         const float pr = exp2_fast(fmaf(s[r], c_log2, L - lam[r >> 2][r & 3]));
@@ -362,22 +377,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
       }
       __builtin_amdgcn_sched_barrier(0x0004);
     }
-    // dV += P^T dO, dK += dS^T Q over this block's two 16-query chunks
+    // the next block's row statistics, then chunk 1's dV / dK products
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (c == 0) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          lamn[rr] = *(const f32x4 *)&lam_s[N1][8 * rr + 4 * g];
-          dln[rr] = *(const f32x4 *)&dlt_s[N1][8 * rr + 4 * g];
-        }
-      }
-      const u32x4 pp = pack8<T>(s, 8 * c);
-      const u32x4 pd = pack8<T>(dp, 8 * c);
+    for (int rr = 0; rr < 4; ++rr) {
+      lamn[rr] = *(const f32x4 *)&lam_s[N1][8 * rr + 4 * g];
+      dln[rr] = *(const f32x4 *)&dlt_s[N1][8 * rr + 4 * g];
+    }
+    {
+      const u32x4 pp = pack8<T>(s, 8);
+      const u32x4 pd = pack8<T>(dp, 8);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dv[db] = Mfma<T>::mac(pp, gt[c][db], dv[db]);
-        dk[db] = Mfma<T>::mac(pd, qt[c][db], dk[db]);
+        dv[db] = Mfma<T>::mac(pp, gt[1][db], dv[db]);
+        dk[db] = Mfma<T>::mac(pd, qt[1][db], dk[db]);
       }
       __builtin_amdgcn_sched_barrier(0x0004);
     }
