@@ -470,7 +470,39 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // ==== fast phase: software pipeline over list entries n_gen .. n_all-1
   const int n_fast = n_all - n_gen;
   auto ftile = [&](int n) __attribute__((always_inline)) { return tile_at(n_gen + n); };
+  // Logit of element r of block (rb, kb) of a fast tile: t = c_log2 * s + lane_off[rb]
+  // (base-2 units), with the ALiBi term's per-register part folded into s.  The
+  // tile lies wholly below (+1) or above (-1) the diagonal for every row of the
+  // workgroup.  fold_max folds the tile starting at key k0 into s (coefficient 0
+  // without ALiBi: no branch, the scores stay in place) and leaves lane_off and
+  // the row max (combined over the lane pair) in mx; `part` selects a quarter of
+  // the elements (0..3) or all of them (-1), so the work can be spread over MFMA
+  // sections.
+  auto fold_max = [&](f32x16 (&sc)[RB][KBN], int k0, int part, float (&lane_off)[RB],
+                      float (&mx)[RB]) __attribute__((always_inline)) {
+    const int adir = k0 + BN - 1 <= q0 ? 1 : -1;
+    const float a = alibi ? adir * sl2c : 0.f;
+    constexpr int NE = 16 * KBN;
+    const int e0 = part < 0 ? 0 : part * NE / 4, e1 = part < 0 ? NE : (part + 1) * NE / 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (part <= 0) {
+        lane_off[rb] = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i[rb]) : 0.f;
+        mx[rb] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        if (e < e0 || e >= e1) continue;
+        const int kb = e / 16, r = e % 16;
+        sc[rb][kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), sc[rb][kb][r]);
+        mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
+      }
+      if (part < 0 || part == 3) mx[rb] = max_lane_pair(fmaf(mx[rb], c_log2, lane_off[rb]));
+    }
+  };
+
   f32x16 sA[RB][KBN], sB[RB][KBN];
+  float loA[RB], mxA[RB], loB[RB], mxB[RB];
   if (n_fast > 0) {
     const int f0 = ftile(0);
     load_tile(f0, K0, Kr);
@@ -478,63 +510,49 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     if (n_fast > 1) load_tile(ftile(1), K1, Kr);
   }
   vm_wait_barrier();
-  if (n_fast > 0) scores(K0, sA);
+  if (n_fast > 0) {
+    scores(K0, sA);
+    fold_max(sA, ftile(0) * BN, -1, loA, mxA);
+  }
   lds_barrier();   // every wave is done with K0 before the first step refills it
 
-  // one step: softmax of tile n (scores in s), scores of tile n+1 (into sn),
-  // O += P V of tile n.  Buffer parity B: K_{n+1} in K[1-B], V_n in V[B].
-  auto fast_step = [&](int n, auto buf, f32x16 (&s)[RB][KBN], f32x16 (&sn)[RB][KBN])
+  // One step: softmax of tile n (folded scores in s, row max in mx), scores of
+  // tile n+1 (into sn) with their fold and max (into lon, mxn), O += P V of
+  // tile n.  Buffer parity B: K_{n+1} in K[1-B], V_n in V[B].
+  auto fast_step = [&](int n, auto buf, f32x16 (&s)[RB][KBN], float (&lo)[RB], float (&mx)[RB],
+                       f32x16 (&sn)[RB][KBN], float (&lon)[RB], float (&mxn)[RB])
                        __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     const uint16_t *kn = B ? K0 : K1;   // K of tile n+1
     const uint16_t *vs = B ? V1 : V0;   // V of tile n
     opaque(ro);
     opaque(to);
+    const int kt1 = n + 1 < n_fast ? ftile(n + 1) : 0;
     if (n + 2 < n_fast) load_tile(ftile(n + 2), B ? K1 : K0, Kr);
-    if (n + 1 < n_fast) load_tile(ftile(n + 1), B ? V0 : V1, Vr);
-    const int k0 = ftile(n) * BN;
-
-    // ALiBi: the tile lies wholly below (+1) or above (-1) the diagonal for
-    // every row of the workgroup; the per-register part of the term is folded
-    // into s (coefficient 0 without ALiBi: no branch, the scores stay in place)
-    const int adir = k0 + BN - 1 <= q0 ? 1 : -1;
-    const float a = alibi ? adir * sl2c : 0.f;
-    float lane_off[RB], mx[RB], off[RB], alpha[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      lane_off[rb] = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i[rb]) : 0.f;
-      mx[rb] = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KBN; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[rb][kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), s[rb][kb][r]);
-          mx[rb] = fmaxf(mx[rb], s[rb][kb][r]);
-        }
-      mx[rb] = fmaf(mx[rb], c_log2, lane_off[rb]);
-      mx[rb] = max_lane_pair(mx[rb]);
-    }
+    if (n + 1 < n_fast) load_tile(kt1, B ? V0 : V1, Vr);
+    float alpha[RB], off[RB];
     update_max(mx, alpha);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) off[rb] = lane_off[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
+    for (int rb = 0; rb < RB; ++rb) off[rb] = lo[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
 
     // Scores of tile n+1 interleaved with the exponentials of tile n, in an
     // order fixed by scheduling fences (only scalar work may cross them): the
-    // first half of the K operand reads up front and the rest one k-step
-    // before they are needed, then per k-step the score products followed by
-    // a share of the exponentials (which do not depend on them), so the
-    // matrix core and the VALU work side by side.  The V^T reads of the first
-    // 16-key chunk go out three quarters in, those of chunk c+1 ahead of the
-    // products of chunk c.  On the last step the scores come from a stale
-    // buffer and are unused.
-    // the matrix-dense part of the step runs at raised issue priority, so the
-    // wave sharing this SIMD fills the gaps with its own VALU work
+    // K operand reads run two k-steps ahead of their products; per k-step the
+    // score products are followed by a share of the exponentials (which do not
+    // depend on them), so the matrix core and the VALU work side by side.  The
+    // V^T reads of the first 16-key chunk go out three quarters in, those of
+    // chunk c+1 ahead of the products of chunk c, and each chunk's P V
+    // products are followed by a quarter of tile n+1's fold and max.  On the
+    // last step the scores come from a stale buffer and are unused.  The
+    // matrix-dense part runs at raised issue priority, so the wave sharing
+    // this SIMD fills the gaps with its own VALU work.
     __builtin_amdgcn_s_setprio(1);
     constexpr int NE = 16 * KBN * RB;    // score elements per lane
     constexpr int EPS = NE / KS;         // exponentials per k-step
+    constexpr int KPF = 2;               // K operand reads run this many k-steps ahead
     u32x4 ka[KS][KBN];
 #pragma unroll
-    for (int t = 0; t < KS / 2; ++t)
+    for (int t = 0; t < KPF; ++t)
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb) ka[t][kb] = read_row_at<D>(kn, 32 * kb, ro[t]);
     __builtin_amdgcn_sched_barrier(0x0004);
@@ -548,11 +566,9 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     u32x4 va[NC][DB];
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      if (t == KS / 2 - 1) {
+      if (t + KPF < KS) {
 #pragma unroll
-        for (int u = KS / 2; u < KS; ++u)
-#pragma unroll
-          for (int kb = 0; kb < KBN; ++kb) ka[u][kb] = read_row_at<D>(kn, 32 * kb, ro[u]);
+        for (int kb = 0; kb < KBN; ++kb) ka[t + KPF][kb] = read_row_at<D>(kn, 32 * kb, ro[t + KPF]);
       }
       if (t == 3 * KS / 4) {
 #pragma unroll
@@ -589,6 +605,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb][db] = Mfma<T>::mac(va[c][db], pk[rb][c], acc[rb][db]);
+      fold_max(sn, kt1 * BN, c * 4 / NC, lon, mxn);
       __builtin_amdgcn_sched_barrier(0x0004);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -597,10 +614,10 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   {
     int n = 0;
     for (; n + 1 < n_fast; n += 2) {
-      fast_step(n, BufIdx<0>{}, sA, sB);
-      fast_step(n + 1, BufIdx<1>{}, sB, sA);
+      fast_step(n, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB);
+      fast_step(n + 1, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA);
     }
-    if (n < n_fast) fast_step(n, BufIdx<0>{}, sA, sB);
+    if (n < n_fast) fast_step(n, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB);
   }
 
   // ---- epilogue: O = acc / l, LSE
