@@ -106,9 +106,11 @@ def cpu_baseline(pr, heads=1):
     sub_do = pr.do[:, :heads].contiguous()
     slopes = pr.alibi_slopes[:heads].clone()
     t0 = time.perf_counter()
-    oracle.attention_fwd(sub_q, sub_k, sub_v, pr.scale, causal=pr.causal, alibi_slopes=slopes)
+    drop = dict(keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed)
+    oracle.attention_fwd(sub_q, sub_k, sub_v, pr.scale, causal=pr.causal, alibi_slopes=slopes,
+                         **drop)
     oracle.attention_bwd(sub_q, sub_k, sub_v, sub_do, pr.scale, causal=pr.causal,
-                         alibi_slopes=slopes)
+                         alibi_slopes=slopes, **drop)
     dt = time.perf_counter() - t0
     pairs = heads * pr.seq_q * (pr.seq_q + 1) // 2
     flops = 14 * pr.head_dim * pairs
@@ -126,6 +128,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--keep-prob", type=float, default=1.0,
+                    help="dropout keep probability (1.0 = no dropout, the headline workload)")
+    ap.add_argument("--dropout-seed", type=int, default=0x5EED)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -152,6 +157,7 @@ def main():
 
     dev = "cuda:0"
     pr = inputs.config(args.config)
+    pr.keep_prob, pr.dropout_seed = args.keep_prob, args.dropout_seed
     q, k, v, do = (t.to(dev) for t in (pr.q, pr.k, pr.v, pr.do))
     kw = fa.problem_kwargs(pr, dev)
     plan = fa.Plan(q, k, heads=pr.heads, layout=pr.layout, **kw)
@@ -203,7 +209,8 @@ def main():
     dom = max(("fwd", "bwd_main", "bwd_post"), key=lambda n: per[n])
     dom_flops = FLOPS_PER_PAIR_D[dom] * D * pairs
     achieved = dom_flops / (per[dom] * 1e-3) / 1e12
-    traffic = traffic_for(dom)
+    # the recorded counters were taken without dropout
+    traffic = traffic_for(dom) if pr.keep_prob >= 1.0 else None
     dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[pr.dtype]
     rec = {
         "metric": METRIC,
@@ -221,7 +228,7 @@ def main():
         "config": {"workload": pr.name, "batch": pr.batch, "heads": pr.heads,
                    "seq_q": pr.seq_q, "seq_k": pr.seq_k, "head_dim": D, "layout": pr.layout,
                    "causal": pr.causal, "pse": "alibi" if pr.alibi_slopes is not None else None,
-                   "pass": "fwd+bwd", "visible_pairs": pairs},
+                   "pass": "fwd+bwd", "visible_pairs": pairs, "keep_prob": pr.keep_prob},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(per["fwd"], 4), "tflops": round(fwd_tf, 2),
                 "pct_of_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},

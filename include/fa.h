@@ -46,6 +46,18 @@
  *                    (the retrieval page's document mask).
  * A query row with no visible key gets O = 0, LSE = -inf, and zero gradient.
  *
+ * Dropout (keep_prob < 1; the guide's section 3.2: the probability of keeping
+ * an element, 1 = no dropout).  It acts on the softmax output: O = (P o M /
+ * keep_prob) V, where M[b,h,i,j] = 1 iff
+ *     philox4x32_10(counter = {j >> 2, i, h, b}, key = {seed & 0xffffffff,
+ *                   seed >> 32}) word (j & 3)  <  floor(keep_prob * 2^32),
+ * Philox4x32 with 10 rounds as published by Salmon, Moraes, Dror and Shaw
+ * ("Parallel random numbers: as easy as 1, 2, 3", SC 2011), seed =
+ * dropout_seed.  LSE is that of the softmax before dropout.  The backward
+ * regenerates M from the same seed (no mask is stored): dV = (P o M /
+ * keep_prob)^T dO, dS = P o (M o (dO V^T) / keep_prob - delta) with
+ * delta_i = sum_d dO_id O_id.  F16/BF16 only.
+ *
  * Bias (pse, added after scaling, never scaled itself):
  *   FA_PSE_ALIBI  bias(h,i,j) = -alibi_slopes[h] * |i - j|, slopes float32 [H].
  *   FA_PSE_DENSE  bias element [b*pse_stride_b + h*pse_stride_h +
@@ -53,9 +65,10 @@
  *
  * Errors: every check runs before any launch; a call that fails validation
  * writes nothing.  FA_ERR_INVALID_ARG: null pointer where one is needed,
- * negative sizes, H*D mismatch, M out of range, bad enum.
- * FA_ERR_UNSUPPORTED: keep_prob != 1, a head_dim the kernels do not cover
- * (F16/BF16: 64 or 128; F32: 32, 64 or 128).  FA_ERR_WORKSPACE: workspace
+ * negative sizes, H*D mismatch, M out of range, bad enum,
+ * keep_prob outside (0, 1].  FA_ERR_UNSUPPORTED: keep_prob < 1 with F32, a
+ * head_dim the kernels do not cover (F16/BF16: 64 or 128; F32: 32, 64 or
+ * 128).  FA_ERR_WORKSPACE: workspace
  * too small.  FA_ERR_HIP: a HIP launch reported an error.
  * Sizes of zero are allowed: B, H or S_q == 0 is a no-op; S_k == 0 makes every
  * row masked (O = 0, LSE = -inf, dQ = 0).
@@ -76,7 +89,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -107,7 +120,7 @@ typedef struct fa_problem {
   int32_t layout;           /* fa_layout */
   int32_t dtype;            /* fa_dtype of Q, K, V, O, dO, dQ, dK, dV */
   float scale;              /* multiplies Q K^T; no default (1/sqrt(D) is usual) */
-  float keep_prob;          /* must be 1.0f: dropout is not supported */
+  float keep_prob;          /* (0, 1]; < 1 applies dropout (see above) */
   uint32_t mask_flags;      /* OR of FA_MASK_* */
   int32_t num_modalities;   /* M, 1..8, for FA_MASK_MODALITY */
   int32_t modality_allow_diag; /* nonzero: i == j is always allowed */
@@ -122,6 +135,7 @@ typedef struct fa_problem {
   const float *alibi_slopes;         /* [H] */
   const void *pse;                   /* dense bias */
   int64_t pse_stride_b, pse_stride_h, pse_stride_q;
+  uint64_t dropout_seed;             /* Philox key when keep_prob < 1 */
 } fa_problem;
 
 /* Forward: O (layout/dtype of Q) and LSE (float32 [B,H,S_q]). */

@@ -26,7 +26,17 @@ one (batch, head) at a time, materialising the whole S_q x S_k score matrix:
 * the backward is the exact gradient of O with respect to Q, K, V given
   dO (the guide's section 2 says the fused operator returns gradients
   without storing the N x N matrix; here that matrix is simply stored,
-  since this is the definition, not the method).
+  since this is the definition, not the method);
+* dropout (``keep_prob`` < 1, section 3.2 parameter table, "retention
+  proportion", default 1.0 = none): the probabilities that multiply V are
+  P_ij * M_ij / keep_prob with M a 0/1 keep mask; the LSE is that of the
+  undropped softmax.  The pages name no generator, so the mask is drawn
+  from Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as
+  1, 2, 3", SC 2011), written here from that paper's definition: word
+  j mod 4 of the output for counter (j div 4, i, h, b) under the 64-bit
+  seed as key; kept iff that word < floor(keep_prob * 2^32) with keep_prob
+  the float32 value.  The gradient is that of the same function with M
+  fixed.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
 closed forms, invariants, finite differences, a library attention routine
@@ -39,7 +49,7 @@ import numpy as np
 __all__ = [
     "bsh_to_bnsd", "bnsd_to_bsh", "allowed", "bias", "head_scores",
     "softmax_rows", "attention_fwd", "attention_bwd", "probabilities",
-    "problem_masks", "problem_fwd", "problem_bwd",
+    "problem_masks", "problem_fwd", "problem_bwd", "philox4x32_10", "dropout_mask",
 ]
 
 
@@ -146,6 +156,49 @@ def softmax_rows(s: np.ndarray):
     return P, lse
 
 
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds (Salmon et al., SC 2011, section 5.2).
+
+    Counter words ``c0..c3`` are integer arrays (broadcast together), the
+    key is two 32-bit integers.  One round: the products M0*c0 and M1*c2
+    are split into high and low halves; the new counter is
+    (hi(M1*c2) ^ c1 ^ key0, lo(M1*c2), hi(M0*c0) ^ c3 ^ key1, lo(M0*c0)).
+    Between rounds the key is advanced by the Weyl constants (the golden
+    ratio and sqrt(3) - 1, scaled to 32 bits).  Returns four uint64 arrays
+    holding 32-bit words."""
+    M0, M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
+    W0, W1 = 0x9E3779B9, 0xBB67AE85
+    x = [np.asarray(c, dtype=np.uint64) & _U32 for c in (c0, c1, c2, c3)]
+    x = list(np.broadcast_arrays(*x))
+    key0, key1 = int(k0) & 0xFFFFFFFF, int(k1) & 0xFFFFFFFF
+    for _ in range(10):
+        p0 = M0 * x[0]            # < 2^64: both factors are below 2^32
+        p1 = M1 * x[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _U32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _U32
+        x = [hi1 ^ x[1] ^ np.uint64(key0), lo1, hi0 ^ x[3] ^ np.uint64(key1), lo0]
+        key0 = (key0 + W0) & 0xFFFFFFFF
+        key1 = (key1 + W1) & 0xFFFFFFFF
+    return x
+
+
+def dropout_mask(b, h, Sq, Sk, keep_prob, seed) -> np.ndarray:
+    """Boolean [Sq, Sk] keep mask of head (b, h); all True when keep_prob >= 1."""
+    kp = float(np.float32(keep_prob))
+    if kp >= 1.0:
+        return np.ones((Sq, Sk), dtype=bool)
+    thr = np.uint64(int(np.floor(kp * 4294967296.0)))
+    i = np.arange(Sq, dtype=np.uint64)[:, None]
+    j4 = np.arange((Sk + 3) // 4, dtype=np.uint64)[None, :]
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    w = philox4x32_10(j4, i, np.uint64(h), np.uint64(b), seed & 0xFFFFFFFF, seed >> 32)
+    words = np.stack(w, axis=-1).reshape(Sq, -1)[:, :Sk]      # key j -> word j % 4
+    return words < thr
+
+
 def _as_f64(x):
     if x is None:
         return None
@@ -182,40 +235,55 @@ def probabilities(q, k, scale, b=0, h=0, **masks) -> np.ndarray:
     return P
 
 
-def attention_fwd(q, k, v, scale, **masks):
+def _drop_scale(b, h, Sq, Sk, keep_prob, seed):
+    """The dropout factor matrix M / keep_prob (float64), or None without dropout."""
+    if float(np.float32(keep_prob)) >= 1.0:
+        return None
+    return dropout_mask(b, h, Sq, Sk, keep_prob, seed) / float(np.float32(keep_prob))
+
+
+def attention_fwd(q, k, v, scale, keep_prob=1.0, dropout_seed=0, **masks):
     """O [B,H,Sq,D] and LSE [B,H,Sq], float64, for BNSD inputs.
 
-    O_i = sum_j P_ij v_j with P the row softmax of
-    scale * q_i . k_j + bias_ij over the allowed keys."""
+    O_i = sum_j P_ij Z_ij v_j with P the row softmax of
+    scale * q_i . k_j + bias_ij over the allowed keys and Z the dropout
+    factors (1 without dropout)."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     mk = _masks(masks)
     B, H, Sq, D = q.shape
+    Sk = k.shape[2]
     O = np.zeros((B, H, Sq, v.shape[3]), dtype=np.float64)
     LSE = np.empty((B, H, Sq), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             P, lse = softmax_rows(head_scores(q, k, scale, b, h, mk))
-            O[b, h] = P @ v[b, h]
+            Z = _drop_scale(b, h, Sq, Sk, keep_prob, dropout_seed)
+            O[b, h] = (P if Z is None else P * Z) @ v[b, h]
             LSE[b, h] = lse
     return O, LSE
 
 
-def attention_bwd(q, k, v, do, scale, **masks):
+def attention_bwd(q, k, v, do, scale, keep_prob=1.0, dropout_seed=0, **masks):
     """dQ, dK, dV (float64, BNSD) of L = sum(O * dO).
 
-    With P the forward probabilities:
-    dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  D_i = sum_j P_ij dP_ij;
-    dS_ij = P_ij (dP_ij - D_i);  dQ_i = scale sum_j dS_ij k_j;
-    dK_j = scale sum_i dS_ij q_i.  The bias has no parameters here."""
+    With P the forward probabilities and Z the dropout factors (1 without
+    dropout): dV_j = sum_i P_ij Z_ij dO_i;  dP_ij = Z_ij dO_i . v_j;
+    D_i = sum_j P_ij dP_ij;  dS_ij = P_ij (dP_ij - D_i);
+    dQ_i = scale sum_j dS_ij k_j;  dK_j = scale sum_i dS_ij q_i.
+    The bias has no parameters here."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     mk = _masks(masks)
-    B, H = q.shape[:2]
+    B, H, Sq = q.shape[:3]
+    Sk = k.shape[2]
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for b in range(B):
         for h in range(H):
             P, _ = softmax_rows(head_scores(q, k, scale, b, h, mk))
-            dv[b, h] = P.T @ do[b, h]
+            Z = _drop_scale(b, h, Sq, Sk, keep_prob, dropout_seed)
+            dv[b, h] = (P if Z is None else P * Z).T @ do[b, h]
             dP = do[b, h] @ v[b, h].T
+            if Z is not None:
+                dP = dP * Z
             Dl = (P * dP).sum(axis=1)
             dS = P * (dP - Dl[:, None])
             dq[b, h] = scale * (dS @ k[b, h])
@@ -237,10 +305,14 @@ def _bnsd(x, p):
     return bsh_to_bnsd(x, p.heads) if p.layout == "BSH" else x
 
 
+def _problem_drop(p) -> dict:
+    return dict(keep_prob=getattr(p, "keep_prob", 1.0), dropout_seed=getattr(p, "dropout_seed", 0))
+
+
 def problem_fwd(p):
     """(O, LSE) for a problem, O in the problem's own layout (float64)."""
     O, LSE = attention_fwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), p.scale,
-                           **problem_masks(p))
+                           **_problem_drop(p), **problem_masks(p))
     return (bnsd_to_bsh(O) if p.layout == "BSH" else O), LSE
 
 
@@ -248,5 +320,5 @@ def problem_bwd(p):
     """(dQ, dK, dV) for a problem with upstream gradient ``p.do``, each in the
     problem's own layout (float64)."""
     g = attention_bwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), _bnsd(p.do, p), p.scale,
-                      **problem_masks(p))
+                      **_problem_drop(p), **problem_masks(p))
     return tuple(bnsd_to_bsh(x) if p.layout == "BSH" else x for x in g)

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.abi_version() == 1
+    assert fa.abi_version() == 2
     assert fa.status_str(0) == "ok"
     assert fa.status_str(-2) == "unsupported configuration"
 
@@ -72,7 +72,11 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
 
 
 @pytest.mark.parametrize("over,code", [
-    ({"keep_prob": 0.9}, fa.FA_ERR_UNSUPPORTED),
+    ({"keep_prob": 0.9, "dtype": fa.FA_F32}, fa.FA_ERR_UNSUPPORTED),
+    ({"keep_prob": 0.0}, fa.FA_ERR_INVALID_ARG),
+    ({"keep_prob": -0.5}, fa.FA_ERR_INVALID_ARG),
+    ({"keep_prob": 1.5}, fa.FA_ERR_INVALID_ARG),
+    ({"keep_prob": float("nan")}, fa.FA_ERR_INVALID_ARG),
     ({"head_dim": 48}, fa.FA_ERR_UNSUPPORTED),
     ({"head_dim": 256}, fa.FA_ERR_UNSUPPORTED),
     ({"dtype": fa.FA_F32, "head_dim": 96}, fa.FA_ERR_UNSUPPORTED),
@@ -123,6 +127,9 @@ def test_workspace_size_and_checks():
     assert st == fa.FA_ERR_WORKSPACE
     st = fa.lib.fa_bwd_post(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert st == fa.FA_ERR_WORKSPACE
-    st = fa.lib.fa_bwd_prep(ctypes.byref(base_problem(keep_prob=0.5)), FAKE, FAKE, FAKE, 1 << 30,
-                            None)
+    st = fa.lib.fa_bwd_prep(ctypes.byref(base_problem(keep_prob=0.5, dtype=fa.FA_F32)), FAKE, FAKE,
+                            FAKE, 1 << 30, None)
     assert st == fa.FA_ERR_UNSUPPORTED
+    st = fa.lib.fa_bwd_prep(ctypes.byref(base_problem(keep_prob=0.0)), FAKE, FAKE, FAKE, 1 << 30,
+                            None)
+    assert st == fa.FA_ERR_INVALID_ARG

@@ -234,3 +234,74 @@ def test_backward_is_bitwise_repeatable():
     g2 = gpu_bwd(pr, o, lse)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------------
+# dropout (keep_prob < 1): the kernels regenerate the Philox keep mask; the oracle
+# draws it from its own Philox
+
+DROP = []
+_dseed = 1000
+for D in (64, 128):
+    for dtype in (torch.bfloat16, torch.float16):
+        for (Sq, Sk) in ((7, 65), (65, 129), (200, 333), (256, 256)):
+            for mask, kp in (("none", 0.9), ("causal", 0.6), ("causal+alibi", 0.8),
+                             ("padding", 0.5)):
+                DROP.append((1, 2, Sq, Sk, D, dtype, "BNSD", mask, kp, _dseed))
+                _dseed += 1
+for mask, kp in (("explicit", 0.7), ("modality+diag", 0.9), ("dense", 0.75),
+                 ("causal+explicit+alibi", 0.2)):
+    DROP.append((2, 3, 97, 150, 64, torch.bfloat16, "BNSD", mask, kp, _dseed))
+    _dseed += 1
+    DROP.append((2, 2, 160, 96, 128, torch.bfloat16, "BSH", mask, kp, _dseed))
+    _dseed += 1
+DROP.append((1, 2, 1024, 1024, 128, torch.bfloat16, "BNSD", "causal+alibi", 0.9, _dseed))
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,kp,seed", DROP,
+                         ids=[f"{c[5]}-D{c[4]}-{c[6]}-{c[2]}x{c[3]}-{c[7]}-kp{c[8]}"
+                              .replace("torch.", "") for c in DROP])
+def test_dropout(B, H, Sq, Sk, D, dtype, layout, mask, kp, seed):
+    pr = make_case(B, H, Sq, Sk, D, dtype, layout, mask, seed)
+    pr.keep_prob = kp
+    pr.dropout_seed = (seed * 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_dropout_mask_is_bit_exact(D):
+    """Q = 0 makes P uniform (1/S_k) and V = I_D (S_k = D) copies P * keep / kp into O,
+    so O * kp * S_k is the 0/1 keep mask itself; likewise dO = I_D (S_q = D) makes
+    dV^T the mask as the key pass draws it."""
+    B, H, kp, seed = 2, 3, 0.5, 0xDEADBEEF12345678
+    S = D
+    eye = torch.eye(D, dtype=torch.bfloat16)
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    k = inputs.randn((B, H, S, D), torch.bfloat16, 77)
+    v = eye.expand(B, H, S, D).contiguous()
+    do = eye.expand(B, H, S, D).contiguous()
+    pr = inputs.Problem("dropmask", B, H, S, S, D, "BNSD", torch.bfloat16, 1.0 / math.sqrt(D),
+                        q, k, v, do, keep_prob=kp, dropout_seed=seed)
+    o, lse = gpu_fwd(pr)
+    dq, dk, dv = gpu_bwd(pr, o, lse)
+    fm = (o.float().cpu() * kp * S).numpy()
+    bm = (dv.float().cpu() * kp * S).numpy()
+    for b in range(B):
+        for h in range(H):
+            want = oracle.dropout_mask(b, h, S, S, kp, seed)
+            assert 0.3 < want.mean() < 0.7
+            np.testing.assert_array_equal(fm[b, h], want.astype(np.float64))
+            np.testing.assert_array_equal(bm[b, h].T, want.astype(np.float64))
+
+
+def test_dropout_seed_changes_the_mask_and_repeats():
+    pr = make_case(1, 2, 130, 130, 64, torch.bfloat16, "BNSD", "causal", 1900)
+    pr.keep_prob = 0.7
+    pr.dropout_seed = 5
+    o1, _ = gpu_fwd(pr)
+    o2, _ = gpu_fwd(pr)
+    assert torch.equal(o1, o2)
+    pr.dropout_seed = 6
+    o3, _ = gpu_fwd(pr)
+    assert not torch.equal(o1, o3)

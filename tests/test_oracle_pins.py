@@ -444,3 +444,128 @@ def test_fully_masked_rows_are_zero_with_minus_inf_lse():
     g2 = oracle.attention_bwd(q, k, v, do2, 1.0, explicit_mask=em)
     for a, b in zip((dq, dk, dv), g2):
         np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------------
+# dropout: the generator, the mask and the dropped attention
+
+def test_philox_known_answer_vectors():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "philox4x32_10_kat.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        v = [int(x, 16) for x in r]
+        got = oracle.philox4x32_10(*v[:6])
+        assert [int(x) for x in got] == v[6:], r
+
+
+def test_dropout_mask_element_rule():
+    # element (i, j) of head (b, h) is word j % 4 of counter (j // 4, i, h, b), taken
+    # here one scalar call at a time, against the vectorised mask
+    b, h, Sq, Sk, seed = 1, 2, 5, 11, 0x0123456789ABCDEF
+    for kp in (0.5, 0.8):
+        m = oracle.dropout_mask(b, h, Sq, Sk, kp, seed)
+        thr = math.floor(float(np.float32(kp)) * 2.0**32)
+        for i in range(Sq):
+            for j in range(Sk):
+                w = oracle.philox4x32_10(j // 4, i, h, b, seed & 0xFFFFFFFF, seed >> 32)
+                assert m[i, j] == (int(w[j % 4]) < thr)
+    # keep_prob 0.5: the threshold is 2^31, so kept <=> the word's top bit is clear
+    m = oracle.dropout_mask(0, 0, 3, 8, 0.5, 7)
+    for i in range(3):
+        for j in range(8):
+            w = int(oracle.philox4x32_10(j // 4, i, 0, 0, 7, 0)[j % 4])
+            assert m[i, j] == ((w >> 31) == 0)
+
+
+@pytest.mark.parametrize("kp", [0.1, 0.5, 0.9])
+def test_dropout_keep_fraction_and_independence(kp):
+    n = 256
+    m = oracle.dropout_mask(0, 0, n, n, kp, 1234)
+    sd = math.sqrt(kp * (1 - kp) / n / n)
+    assert abs(m.mean() - kp) < 6 * sd
+    # another head, batch or seed gives an independent mask: agreement rate kp^2 + (1-kp)^2
+    agree = kp * kp + (1 - kp) * (1 - kp)
+    sd2 = math.sqrt(agree * (1 - agree) / n / n)
+    for other in (oracle.dropout_mask(0, 1, n, n, kp, 1234), oracle.dropout_mask(1, 0, n, n, kp, 1234),
+                  oracle.dropout_mask(0, 0, n, n, kp, 1235)):
+        assert abs((m == other).mean() - agree) < 6 * sd2
+    # the four words of one counter are not tied to each other
+    c = np.array([m[:, j::4].mean() for j in range(4)])
+    assert np.all(np.abs(c - kp) < 6 * math.sqrt(kp * (1 - kp) / (n * n / 4)))
+
+
+def test_keep_prob_one_is_bit_identical_to_no_dropout():
+    q, k, v, do = rnd((2, 2, 6, 3), 151), rnd((2, 2, 7, 3), 152), rnd((2, 2, 7, 3), 153), \
+        rnd((2, 2, 6, 3), 154)
+    a = oracle.attention_fwd(q, k, v, 0.7, causal=True)
+    b = oracle.attention_fwd(q, k, v, 0.7, keep_prob=1.0, dropout_seed=99, causal=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    ga = oracle.attention_bwd(q, k, v, do, 0.7, causal=True)
+    gb = oracle.attention_bwd(q, k, v, do, 0.7, keep_prob=1.0, dropout_seed=99, causal=True)
+    for x, y in zip(ga, gb):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_dropout_forward_bruteforce():
+    # O_i = sum_j P_ij * keep_ij / kp * v_j term by term; LSE is the undropped one
+    B, H, Sq, Sk, D, kp, seed = 1, 2, 5, 9, 3, 0.6, 42
+    q, k, v = rnd((B, H, Sq, D), 161), rnd((B, H, Sk, D), 162), rnd((B, H, Sk, D), 163)
+    O, L = oracle.attention_fwd(q, k, v, 0.8, keep_prob=kp, dropout_seed=seed, causal=True)
+    _, L0 = oracle.attention_fwd(q, k, v, 0.8, causal=True)
+    np.testing.assert_array_equal(L, L0)
+    for h in range(H):
+        P = oracle.probabilities(q, k, 0.8, 0, h, causal=True)
+        M = oracle.dropout_mask(0, h, Sq, Sk, kp, seed)
+        for i in range(Sq):
+            for d in range(D):
+                want = math.fsum(P[i, j] * (1.0 / float(np.float32(kp)) if M[i, j] else 0.0)
+                                 * v[0, h, j, d] for j in range(Sk))
+                assert abs(O[0, h, i, d] - want) < 1e-13
+
+
+def test_dropout_is_unbiased_over_seeds():
+    # E over seeds of the dropped output is the undropped output (the 1/kp scaling)
+    B, H, Sq, Sk, D, kp = 1, 1, 3, 6, 2, 0.7
+    q, k, v = rnd((B, H, Sq, D), 171), rnd((B, H, Sk, D), 172), rnd((B, H, Sk, D), 173)
+    O0, _ = oracle.attention_fwd(q, k, v, 1.0)
+    n = 3000
+    acc = np.zeros_like(O0)
+    for s in range(n):
+        acc += oracle.attention_fwd(q, k, v, 1.0, keep_prob=kp, dropout_seed=s * 7919 + 1)[0]
+    P = oracle.probabilities(q, k, 1.0)
+    var = (P ** 2) @ (v[0, 0] ** 2) * (1.0 / kp - 1.0)          # per-element variance
+    err = np.abs(acc / n - O0)[0, 0]
+    assert np.all(err < 6 * np.sqrt(var / n) + 1e-12), (err, np.sqrt(var / n))
+
+
+@pytest.mark.parametrize("masks", [dict(), dict(causal=True, alibi_slopes=np.array([0.4, 0.2]))],
+                         ids=["plain", "causal_alibi"])
+def test_dropout_backward_central_differences(masks):
+    B, H, Sq, Sk, D, kp, seed = 1, 2, 4, 6, 3, 0.6, 2024
+    q, k, v, do = rnd((B, H, Sq, D), 181), rnd((B, H, Sk, D), 182), rnd((B, H, Sk, D), 183), \
+        rnd((B, H, Sq, D), 184)
+    scale = 0.55
+
+    def loss(q_, k_, v_):
+        O, _ = oracle.attention_fwd(q_, k_, v_, scale, keep_prob=kp, dropout_seed=seed, **masks)
+        return float((O * do).sum())
+
+    grads = oracle.attention_bwd(q, k, v, do, scale, keep_prob=kp, dropout_seed=seed, **masks)
+    # the mask really drops something here, and the gradient differs from the undropped one
+    assert not oracle.dropout_mask(0, 0, Sq, Sk, kp, seed).all()
+    g0 = oracle.attention_bwd(q, k, v, do, scale, **masks)
+    assert not np.allclose(grads[2], g0[2])
+    eps = 1e-6
+    for which, g in zip(range(3), grads):
+        base = [q, k, v]
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (which, idx, fd, g[idx])

@@ -59,6 +59,7 @@ class FaProblem(ctypes.Structure):
         ("pse_stride_b", ctypes.c_int64),
         ("pse_stride_h", ctypes.c_int64),
         ("pse_stride_q", ctypes.c_int64),
+        ("dropout_seed", ctypes.c_uint64),
     ]
 
 
@@ -123,7 +124,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
                  modality_allow_diag: bool = False,
                  key_valid: Optional[torch.Tensor] = None,
                  alibi_slopes: Optional[torch.Tensor] = None,
-                 pse: Optional[torch.Tensor] = None):
+                 pse: Optional[torch.Tensor] = None, dropout_seed: int = 0):
     """Build an ``FaProblem`` from tensors (shape checks only).  Returns the
     struct and the list of tensors whose memory it references."""
     if layout not in _LAYOUTS:
@@ -153,6 +154,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
     p.dtype = _DTYPES[q.dtype]
     p.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     p.keep_prob = float(keep_prob)
+    p.dropout_seed = int(dropout_seed) & 0xFFFFFFFFFFFFFFFF
     keep = []
     flags = 0
     if causal:
@@ -309,4 +311,5 @@ def problem_kwargs(pr, device) -> dict:
     return dict(scale=pr.scale, causal=pr.causal, explicit_mask=mv(pr.explicit_mask),
                 q_modality=mv(pr.q_modality), k_modality=mv(pr.k_modality),
                 modality_allow=pr.modality_allow, modality_allow_diag=pr.modality_allow_diag,
-                key_valid=mv(pr.key_valid), alibi_slopes=mv(pr.alibi_slopes), pse=mv(pr.pse))
+                key_valid=mv(pr.key_valid), alibi_slopes=mv(pr.alibi_slopes), pse=mv(pr.pse),
+                keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed)

@@ -32,7 +32,8 @@ fa_status check_problem(const fa_problem *p) {
   if (p->layout != FA_BNSD && p->layout != FA_BSH) return FA_ERR_INVALID_ARG;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
-  if (p->keep_prob != 1.0f) return FA_ERR_UNSUPPORTED;
+  if (!(p->keep_prob > 0.f && p->keep_prob <= 1.f)) return FA_ERR_INVALID_ARG;   // NaN too
+  if (p->keep_prob < 1.f && p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
   const uint32_t known = FA_MASK_CAUSAL | FA_MASK_EXPLICIT | FA_MASK_MODALITY | FA_MASK_PADDING;
   if (p->mask_flags & ~known) return FA_ERR_INVALID_ARG;
@@ -112,6 +113,14 @@ Params make_params(const fa_problem *p) {
   r.alibi_slopes = p->alibi_slopes;
   r.pse = p->pse;
   r.pse_sb = p->pse_stride_b; r.pse_sh = p->pse_stride_h; r.pse_sq = p->pse_stride_q;
+  if (p->keep_prob < 1.f) {
+    // keep iff word < floor(keep_prob * 2^32); keep_prob * 2^32 is exact in double
+    r.dropout = 1;
+    r.drop_thr = (uint32_t)floor((double)p->keep_prob * 4294967296.0);
+    r.seed_lo = (uint32_t)(p->dropout_seed & 0xffffffffu);
+    r.seed_hi = (uint32_t)(p->dropout_seed >> 32);
+    r.inv_keep = 1.f / p->keep_prob;
+  }
   return r;
 }
 

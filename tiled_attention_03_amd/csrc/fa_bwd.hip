@@ -45,7 +45,9 @@ constexpr int KBQ = 64;     // keys per step, query pass
 
 // ===========================================================================
 // key pass: dK, dV
-template <typename T, int D>
+// DROP: dropout compiled in (keep_prob < 1); the kernel without it carries no
+// dropout code at all.
+template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   // per step with per-wave classification.  The sums over blocks do not
   // depend on the order.
   int f0 = it_end, f1 = it_end;
-  if (!f_elem && !dense && j0 + KB <= p.Sk) {
+  if (!f_elem && !dense && !DROP && j0 + KB <= p.Sk) {
     const int first = (causal || alibi) ? max(it_begin, (j0 + KB - 1 + QB - 1) / QB) : it_begin;
     const int last = p.Sq / QB;   // full blocks only
     if (first < last) { f0 = first; f1 = last; }
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     // per-element work) or general.  Blocks the mask hides wholly take the
     // general path, which yields P = dS = 0; keeping the accumulation
     // unconditional lets the dK/dV accumulators stay in place.
-    bool general = f_elem || dense || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
+    bool general = f_elem || dense || DROP || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
     if (causal && jw + 31 > i0) general = true;
     if (alibi && !(i0 >= jw + 31)) general = true;   // fast ALiBi form needs i >= j
     {
@@ -209,15 +211,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
             const int i = i0 + 8 * rr + 4 * g + q;
             bool ok = i < p.Sq && my_j < p.Sk;
             if (ok) ok = allowed_elem(p, b, h, i, my_j);
-            float pr = 0.f;
+            float pr = 0.f, m = 1.f;
             if (ok) {
               float t = s[r] * c_log2;
               if (alibi) t -= sl2 * fabsf((float)(i - my_j));
               else if (dense) t += dense_bias(p, b, h, i, my_j) * kLog2e;
               pr = exp2_fast(t - ls[q]);
+              if (DROP) m = dropout_factor(p, b, h, i, my_j);
             }
-            s[r] = pr;
-            dp[r] = pr * (dp[r] - dl[q]);
+            // dropout: P o M / keep_prob feeds dV, and dP is masked the same way
+            s[r] = pr * m;
+            dp[r] = pr * (dp[r] * m - dl[q]);
           }
         }
       }
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 
 // ===========================================================================
 // query pass: dQ
-template <typename T, int D>
+template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     // fast or general tile; tiles hidden from this wave (at most one per
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
     // accumulation stays unconditional
-    bool general = f_elem || dense || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq);
+    bool general = f_elem || dense || DROP || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq);
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
     {
@@ -554,14 +558,15 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
             const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
             bool ok = j < p.Sk && my_i < p.Sq;
             if (ok) ok = allowed_elem(p, b, h, my_i, j);
-            float pr = 0.f;
+            float pr = 0.f, m = 1.f;
             if (ok) {
               float t = s[r] * c_log2;
               if (alibi) t -= sl2 * fabsf((float)(my_i - j));
               else if (dense) t += dense_bias(p, b, h, my_i, j) * kLog2e;
               pr = exp2_fast(t - lse2);
+              if (DROP) m = dropout_factor(p, b, h, my_i, j);
             }
-            dp[r] = pr * (dp[r] - dlt);
+            dp[r] = pr * (dp[r] * m - dlt);   // dropout masks dP like P
           }
         }
         // dQ^T += K^T . dS^T over this block's two 16-key chunks
@@ -602,8 +607,12 @@ hipError_t launch_kv(const Params &p, hipStream_t s) {
   const int n_ktiles = (p.Sk + KB - 1) / KB;
   const int64_t blocks = (int64_t)n_ktiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s, p,
-                     n_ktiles);
+  if (p.dropout)
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, true>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
+                       p, n_ktiles);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, false>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
+                       p, n_ktiles);
   return hipGetLastError();
 }
 
@@ -612,8 +621,12 @@ hipError_t launch_q(const Params &p, hipStream_t s) {
   const int n_qtiles = (p.Sq + QBQ - 1) / QBQ;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_q_kernel<T, D>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s, p,
-                     n_qtiles);
+  if (p.dropout)
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, true>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
+                       p, n_qtiles);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, false>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
+                       p, n_qtiles);
   return hipGetLastError();
 }
 

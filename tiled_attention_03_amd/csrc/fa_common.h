@@ -53,7 +53,54 @@ struct Params {
   const float *alibi_slopes;
   const void *pse;
   int64_t pse_sb, pse_sh, pse_sq;
+  // dropout (keep_prob < 1): keep iff a Philox word < drop_thr; kept
+  // probabilities are scaled by inv_keep
+  int dropout;
+  uint32_t drop_thr;
+  uint32_t seed_lo, seed_hi;
+  float inv_keep;
 };
+
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): each round multiplies counter words
+// 0 and 2 by the round constants, and the new counter is (hi(w2*M1) ^ c1 ^ k0,
+// lo(w2*M1), hi(w0*M0) ^ c3 ^ k1, lo(w0*M0)); the key is bumped by the Weyl
+// constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
+    const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// The dropout words of keys 4*(j/4) .. 4*(j/4) + 3 for query i of head (b, h):
+// the Philox output for counter (j/4, i, h, b); word j % 4 belongs to key j.
+__device__ __forceinline__ void dropout_words(const Params &p, int b, int h, int i, int j,
+                                              uint32_t (&w)[4]) {
+  w[0] = (uint32_t)(j >> 2);
+  w[1] = (uint32_t)i;
+  w[2] = (uint32_t)h;
+  w[3] = (uint32_t)b;
+  philox4x32_10(w, p.seed_lo, p.seed_hi);
+}
+
+// Factor that multiplies probability (i, j) in P V and in dP: inv_keep if the
+// element is kept, else 0.
+__device__ __forceinline__ float dropout_factor(const Params &p, int b, int h, int i, int j) {
+  uint32_t w[4];
+  dropout_words(p, b, h, i, j, w);
+  return w[j & 3] < p.drop_thr ? p.inv_keep : 0.f;
+}
 
 // ------------------------------------------------------------------------
 // element conversion

@@ -79,7 +79,9 @@ struct FwdCfg {
 // Tile class for one wave: what the wave does with the tile's scores.
 enum : int { kFast = 0, kGeneral = 1, kDead = 2 };
 
-template <typename T, int D, int NW, int RB_, int KBN_>
+// DROP: dropout compiled in (keep_prob < 1); without it the kernel carries no
+// dropout code.
+template <typename T, int D, int NW, int RB_, int KBN_, bool DROP>
 __global__ __launch_bounds__(NW * 64, (FwdCfg<T, D, NW, RB_, KBN_>::OCC))
 void fwd_mfma_kernel(Params p, int n_qtiles) {
   using C = FwdCfg<T, D, NW, RB_, KBN_>;
@@ -207,7 +209,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // 1 generic, 2 fast (no per-element work for any wave of the workgroup).
   auto wg_class = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BN;
-    bool fast = !dense && !f_exp && k0 + BN <= p.Sk;
+    bool fast = !dense && !f_exp && !DROP && k0 + BN <= p.Sk;
     if (causal && k0 + BN - 1 > q0) fast = false;
     if (alibi && !(k0 + BN - 1 <= q0 || (!causal && k0 >= q0 + C::BM - 1))) fast = false;
     if (f_pad || f_mod) {
@@ -444,6 +446,19 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
             part[r & 3] += x;
           }
         l_run[rb] = l_run[rb] * alpha[rb] + ((part[0] + part[1]) + (part[2] + part[3]));
+        if (DROP) {
+          // P o M / keep_prob enters P V; the row sum above is taken before dropout
+#pragma unroll
+          for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              uint32_t wd[4];
+              dropout_words(p, b, h, my_i[rb], k0 + 32 * kb + 8 * rr + 4 * g, wd);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                s[rb][kb][4 * rr + q] *= wd[q] < p.drop_thr ? p.inv_keep : 0.f;
+            }
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) pk[rb][c] = pack8<T>(s[rb][c >> 1], 8 * (c & 1));
       }
@@ -652,8 +667,12 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
   const int n_qtiles = (p.Sq + C::BM - 1) / C::BM;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN>), dim3((unsigned)blocks), dim3(C::NT), 0, s,
-                     p, n_qtiles);
+  if (p.dropout)
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN, true>), dim3((unsigned)blocks),
+                       dim3(C::NT), 0, s, p, n_qtiles);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN, false>), dim3((unsigned)blocks),
+                       dim3(C::NT), 0, s, p, n_qtiles);
   return hipGetLastError();
 }
 

@@ -91,6 +91,8 @@ class Problem:
     key_valid: Optional[torch.Tensor] = None          # bool [B,Sk]
     alibi_slopes: Optional[torch.Tensor] = None       # float32 [H]
     pse: Optional[torch.Tensor] = None                # float32, broadcastable to [B,H,Sq,Sk]
+    keep_prob: float = 1.0                            # < 1: dropout after the softmax
+    dropout_seed: int = 0                             # Philox key of the dropout mask
     meta: dict = field(default_factory=dict)
 
 
