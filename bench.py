@@ -30,7 +30,9 @@ KERNEL_SOURCES = {   # files whose text decides each timed kernel's code
     "fwd": [_CSRC + f for f in ("fa_fwd.hip", "fa_tile.h", "fa_common.h")],
     "bwd_main": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
     "bwd_post": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
+    "maxsim": [_CSRC + f for f in ("fa_maxsim.hip", "fa_tile.h", "fa_common.h")],
 }
+MAXSIM_METRIC = "MaxSim late-interaction scores/s on 1 MI355X and % of HBM peak"
 # Algorithmic flops per visible (query, key) pair, in units of D, per timed call:
 # forward Q K^T and P V; the key pass (bwd_main) recomputes Q K^T and forms
 # dO V^T, P^T dO and dS^T Q; the query pass (bwd_post) adds dS K (its own
@@ -120,6 +122,80 @@ def cpu_baseline(pr, heads=1):
                       f"numpy float64, algorithmic flops 14*D per visible pair"}
 
 
+def maxsim_bytes(case) -> int:
+    """Bytes the MaxSim result depends on: every query row, the valid document
+    rows, the document mask, and the outputs (rowmax float32, score float32)."""
+    B, Lq, D = case.q.shape
+    Ld = case.d.shape[1]
+    valid_docs = int(case.d_valid.sum()) if case.d_valid is not None else B * Ld
+    es = case.q.element_size()
+    mask = B * Ld if case.d_valid is not None else 0
+    return B * Lq * D * es + valid_docs * D * es + mask + B * Lq * 4 + B * 4
+
+
+def bench_maxsim(args):
+    """The MaxSim kernel on the late-interaction workload's own tensors."""
+    import torch
+    from tiled_attention_03_amd import binding as fa
+    from tiled_attention_03_amd import inputs
+
+    case = inputs.maxsim_workload()
+    dev = "cuda:0"
+    q, d = case.q.to(dev), case.d.to(dev)
+    dv = case.d_valid.to(dev)
+    B, Lq, D = q.shape
+    rm = torch.empty(B, Lq, dtype=torch.float32, device=dev)
+    sc = torch.empty(B, dtype=torch.float32, device=dev)
+    dv = fa._as_bytes(dv)                     # the mask as bytes once, outside the timed calls
+    call = lambda: fa.maxsim(q, d, d_valid=dv, rowmax=rm, score=sc)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    nbytes = maxsim_bytes(case)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_for("maxsim")
+    rec = {
+        "metric": MAXSIM_METRIC, "value": round(B / (ms * 1e-3), 1), "unit": "scores/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": B, "len_q": Lq, "len_d": d.shape[1],
+                   "dim": D, "valid_docs": int(case.d_valid.sum())},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"kernel": "maxsim", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:  # pragma: no cover - reporting only
+            threads = os.cpu_count() or 1
+        # the whole workload, repeated for about ten seconds
+        reps, t0 = 0, time.perf_counter()
+        while reps < 100 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+            oracle.maxsim(case.q, case.d, None, case.d_valid)
+            reps += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(reps * B / dt, 2), "unit": "scores/s",
+                               "cores": int(threads), "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"the whole workload ({B} samples) x {reps}, numpy "
+                                         f"float64"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +207,9 @@ def main():
     ap.add_argument("--keep-prob", type=float, default=1.0,
                     help="dropout keep probability (1.0 = no dropout, the headline workload)")
     ap.add_argument("--dropout-seed", type=int, default=0x5EED)
+    ap.add_argument("--workload", choices=("attention", "maxsim"), default="attention",
+                    help="attention: the fused attention step (the headline); maxsim: the "
+                         "late-interaction MaxSim kernel")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -150,6 +229,10 @@ def main():
               "(every (batch, head) is independent: shard heads across GPUs and run this "
               "per GPU).", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "maxsim":
+        bench_maxsim(args)
+        return
 
     import torch
     from tiled_attention_03_amd import binding as fa

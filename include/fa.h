@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_OK = 0,
@@ -173,6 +173,46 @@ fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const v
 fa_status fa_bwd_post(const fa_problem *p, const void *q, const void *k, const void *v,
                       const float *lse, const void *dout, void *dq,
                       const void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MaxSim late-interaction score (retrieval page, "Layer 2: semantic
+ * modelling"): for sample b, the similarity of query token i and document
+ * token j is the plain dot product sim_ij = q_i . d_j over the embedding
+ * width (no scale, no softmax).  Invalid document tokens are excluded
+ * (-inf); each query token keeps its best match, rowmax_i = max_j sim_ij; the
+ * score is the sum of rowmax over the valid query tokens divided by L_q.
+ *
+ *   q [B, L_q, D], d [B, L_d, D]: contiguous rows, dtype FA_BF16 or FA_F16,
+ *       device pointers, 16-byte aligned (d may be NULL when L_d == 0);
+ *   q_valid [B, L_q], d_valid [B, L_d]: uint8, nonzero = real token; NULL
+ *       means every token is real;
+ *   rowmax float32 [B, L_q] (may be NULL when L_q == 0): -inf for an invalid
+ *       query token and for a query token with no valid document token;
+ *   score float32 [B] (may be NULL when B == 0): the sum over valid query
+ *       tokens of rowmax, divided by L_q; 0 when no query token is valid
+ *       (including L_q == 0); -inf when a valid query token sees no valid
+ *       document token.
+ *
+ * The dot products are accumulated in float32 from exact products; the
+ * result is bitwise repeatable.  Errors: FA_ERR_INVALID_ARG for a null
+ * struct, negative sizes, a bad dtype enum, pad0 != 0, or a
+ * missing/misaligned tensor; FA_ERR_UNSUPPORTED for FA_F32, D not a multiple
+ * of 128 or above 1024, or L_d above 16384.  B == 0 is a no-op.
+ * Synchronisation as for the attention entry points; no workspace.
+ * ------------------------------------------------------------------------ */
+typedef struct fa_maxsim_problem {
+  int32_t batch;            /* B */
+  int32_t len_q;            /* L_q */
+  int32_t len_d;            /* L_d */
+  int32_t dim;              /* D, the embedding width */
+  int32_t dtype;            /* fa_dtype of q and d */
+  int32_t pad0;             /* must be 0 */
+  const uint8_t *q_valid;   /* [B, L_q] or NULL */
+  const uint8_t *d_valid;   /* [B, L_d] or NULL */
+} fa_maxsim_problem;
+
+fa_status fa_maxsim(const fa_maxsim_problem *p, const void *q, const void *d, float *rowmax,
+                    float *score, hipStream_t stream);
 
 const char *fa_status_str(fa_status s);
 int fa_abi_version(void);

@@ -38,6 +38,15 @@ one (batch, head) at a time, materialising the whole S_q x S_k score matrix:
   the float32 value.  The gradient is that of the same function with M
   fixed.
 
+The MaxSim late-interaction score (retrieval page, "Layer 2: semantic
+modelling") is :func:`maxsim`: plain dot products of query and document
+token embeddings, invalid document tokens excluded, the best match of each
+query token, summed over the query tokens and divided by L_q.  The page's
+code sets a whole invalid query row to -inf and then sums every row, which
+makes the score -inf as soon as one query token is padding; here that row's
+max is reported as -inf but left out of the sum (the divisor stays L_q, as
+printed).
+
 Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
 closed forms, invariants, finite differences, a library attention routine
 on sliced problems).  Nothing here is "parity unpinned".
@@ -49,7 +58,7 @@ import numpy as np
 __all__ = [
     "bsh_to_bnsd", "bnsd_to_bsh", "allowed", "bias", "head_scores",
     "softmax_rows", "attention_fwd", "attention_bwd", "probabilities",
-    "problem_masks", "problem_fwd", "problem_bwd", "philox4x32_10", "dropout_mask",
+    "problem_masks", "problem_fwd", "problem_bwd", "philox4x32_10", "dropout_mask", "maxsim",
 ]
 
 
@@ -322,3 +331,29 @@ def problem_bwd(p):
     g = attention_bwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), _bnsd(p.do, p), p.scale,
                       **_problem_drop(p), **problem_masks(p))
     return tuple(bnsd_to_bsh(x) if p.layout == "BSH" else x for x in g)
+
+
+def maxsim(q, d, q_valid=None, d_valid=None):
+    """MaxSim of each sample: (rowmax [B, L_q], score [B]), float64.
+
+    q [B, L_q, D] and d [B, L_d, D]; q_valid [B, L_q] and d_valid [B, L_d]
+    are booleans (None = all valid).  sim_ij = q_i . d_j; invalid documents
+    are -inf; rowmax_i = max_j sim_ij, -inf for an invalid query token or
+    when no document token is valid; score = (sum of rowmax over valid
+    query tokens) / L_q, and 0 when there is no valid query token."""
+    q, d = _as_f64(q), _as_f64(d)
+    B, Lq = q.shape[:2]
+    Ld = d.shape[1]
+    qv = np.ones((B, Lq), dtype=bool) if q_valid is None else np.asarray(_as_np(q_valid), dtype=bool)
+    dv = np.ones((B, Ld), dtype=bool) if d_valid is None else np.asarray(_as_np(d_valid), dtype=bool)
+    rowmax = np.full((B, Lq), -np.inf)
+    score = np.zeros(B)
+    for b in range(B):
+        sim = q[b] @ d[b].T                                  # [L_q, L_d]
+        sim = np.where(dv[b][None, :], sim, -np.inf)
+        rm = sim.max(axis=1) if Ld > 0 else np.full(Lq, -np.inf)
+        rm = np.where(qv[b], rm, -np.inf)
+        rowmax[b] = rm
+        if Lq > 0:
+            score[b] = rm[qv[b]].sum() / Lq
+    return rowmax, score

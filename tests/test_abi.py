@@ -33,25 +33,27 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.abi_version() == 2
+    assert fa.abi_version() == 3
     assert fa.status_str(0) == "ok"
     assert fa.status_str(-2) == "unsupported configuration"
 
 
-def test_struct_layout_matches_c(tmp_path):
-    fields = [f[0] for f in fa.FaProblem._fields_]
+@pytest.mark.parametrize("cls,cname", [(fa.FaProblem, "fa_problem"),
+                                       (fa.FaMaxsimProblem, "fa_maxsim_problem")])
+def test_struct_layout_matches_c(tmp_path, cls, cname):
+    fields = [f[0] for f in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(fa_problem, {f}));' for f in fields)
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof({cname}, {f}));' for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\nint main(void){\n'
-                   + body + '\n  printf("sizeof %zu\\n", sizeof(fa_problem));\n  return 0;\n}\n')
+                   + body + f'\n  printf("sizeof %zu\\n", sizeof({cname}));\n  return 0;\n}}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", "-I/opt/rocm/include",
                     str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
     got = dict(line.split() for line in out.strip().splitlines())
     for f in fields:
-        assert int(got[f]) == getattr(fa.FaProblem, f).offset, f
-    assert int(got["sizeof"]) == ctypes.sizeof(fa.FaProblem)
+        assert int(got[f]) == getattr(cls, f).offset, f
+    assert int(got["sizeof"]) == ctypes.sizeof(cls)
 
 
 def base_problem(**over):
@@ -133,3 +135,45 @@ def test_workspace_size_and_checks():
     st = fa.lib.fa_bwd_prep(ctypes.byref(base_problem(keep_prob=0.0)), FAKE, FAKE, FAKE, 1 << 30,
                             None)
     assert st == fa.FA_ERR_INVALID_ARG
+
+
+def maxsim_problem(**over):
+    p = fa.FaMaxsimProblem()
+    p.batch, p.len_q, p.len_d, p.dim, p.dtype = 4, 32, 256, 768, fa.FA_BF16
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+def call_maxsim(p, q=FAKE, d=FAKE, rowmax=FAKE, score=FAKE):
+    return fa.lib.fa_maxsim(ctypes.byref(p), q, d, rowmax, score, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"dtype": fa.FA_F32}, fa.FA_ERR_UNSUPPORTED),
+    ({"dim": 64}, fa.FA_ERR_UNSUPPORTED),
+    ({"dim": 768 + 64}, fa.FA_ERR_UNSUPPORTED),
+    ({"dim": 1152}, fa.FA_ERR_UNSUPPORTED),
+    ({"len_d": 16385}, fa.FA_ERR_UNSUPPORTED),
+    ({"batch": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"len_q": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"len_d": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"dim": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"dtype": 7}, fa.FA_ERR_INVALID_ARG),
+    ({"pad0": 1}, fa.FA_ERR_INVALID_ARG),
+])
+def test_maxsim_validation_codes(over, code):
+    assert call_maxsim(maxsim_problem(**over)) == code
+
+
+def test_maxsim_pointer_checks():
+    p = maxsim_problem()
+    assert call_maxsim(p, q=None) == fa.FA_ERR_INVALID_ARG
+    assert call_maxsim(p, d=None) == fa.FA_ERR_INVALID_ARG
+    assert call_maxsim(p, rowmax=None) == fa.FA_ERR_INVALID_ARG
+    assert call_maxsim(p, score=None) == fa.FA_ERR_INVALID_ARG
+    assert call_maxsim(p, d=ctypes.c_void_p((1 << 20) + 8)) == fa.FA_ERR_INVALID_ARG
+    assert call_maxsim(p, score=ctypes.c_void_p((1 << 20) + 2)) == fa.FA_ERR_INVALID_ARG
+    assert fa.lib.fa_maxsim(None, FAKE, FAKE, FAKE, FAKE, None) == fa.FA_ERR_INVALID_ARG
+    # B == 0 is a no-op that needs no pointers
+    assert call_maxsim(maxsim_problem(batch=0), q=None, d=None, rowmax=None, score=None) == 0

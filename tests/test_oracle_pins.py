@@ -569,3 +569,130 @@ def test_dropout_backward_central_differences(masks):
             minus[which][idx] -= eps
             fd = (loss(*plus) - loss(*minus)) / (2 * eps)
             assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (which, idx, fd, g[idx])
+
+
+# ----------------------------------------------------------------------------------
+# MaxSim (retrieval page, "Layer 2: semantic modelling")
+
+def _maxsim_bruteforce(q, d, qv, dv):
+    """Term by term: math.fsum dot products, the mask rules written out."""
+    B, Lq, D = q.shape
+    Ld = d.shape[1]
+    rows, scores = [], []
+    for b in range(B):
+        rm = []
+        for i in range(Lq):
+            best = -math.inf
+            for j in range(Ld):
+                if dv[b][j]:
+                    best = max(best, math.fsum(float(q[b, i, k]) * float(d[b, j, k])
+                                               for k in range(D)))
+            rm.append(best if qv[b][i] else -math.inf)
+        rows.append(rm)
+        kept = [rm[i] for i in range(Lq) if qv[b][i]]
+        scores.append(math.fsum(kept) / Lq if Lq else 0.0)
+    return rows, scores
+
+
+@pytest.mark.parametrize("Lq,Ld,D", [(1, 1, 1), (3, 5, 4), (6, 2, 3), (4, 7, 8)])
+def test_maxsim_bruteforce(Lq, Ld, D):
+    rng = np.random.default_rng(Lq * 100 + Ld * 10 + D)
+    B = 3
+    q, d = rng.standard_normal((B, Lq, D)), rng.standard_normal((B, Ld, D))
+    qv, dv = rng.random((B, Lq)) < 0.8, rng.random((B, Ld)) < 0.7
+    dv[0] = True                       # one sample with every document valid
+    dv[2] = False                      # and one with none
+    rows, scores = _maxsim_bruteforce(q, d, qv, dv)
+    rm, sc = oracle.maxsim(q, d, qv, dv)
+    for b in range(B):
+        for i in range(Lq):
+            if math.isinf(rows[b][i]):
+                assert rm[b, i] == rows[b][i]
+            else:
+                assert abs(rm[b, i] - rows[b][i]) < 1e-12
+        if math.isinf(scores[b]):
+            assert sc[b] == scores[b]
+        else:
+            assert abs(sc[b] - scores[b]) < 1e-12
+
+
+def test_maxsim_closed_forms():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 6))
+    # documents = the standard basis: the best match of q_i is its largest component
+    d = np.broadcast_to(np.eye(6), (2, 6, 6)).copy()
+    rm, sc = oracle.maxsim(q, d)
+    np.testing.assert_array_equal(rm, q.max(axis=2))
+    np.testing.assert_allclose(sc, q.max(axis=2).sum(axis=1) / 4, rtol=0, atol=1e-15)
+    # one document: rowmax is that dot product
+    d1 = rng.standard_normal((2, 1, 6))
+    rm, _ = oracle.maxsim(q, d1)
+    for b in range(2):
+        for i in range(4):
+            assert abs(rm[b, i] - sum(q[b, i, k] * d1[b, 0, k] for k in range(6))) < 1e-13
+    # zero queries score 0 against any valid documents
+    rm, sc = oracle.maxsim(np.zeros((2, 4, 6)), rng.standard_normal((2, 5, 6)))
+    assert np.all(rm == 0) and np.all(sc == 0)
+
+
+def test_maxsim_invariants():
+    rng = np.random.default_rng(6)
+    B, Lq, Ld, D = 2, 5, 9, 7
+    q, d = rng.standard_normal((B, Lq, D)), rng.standard_normal((B, Ld, D))
+    dv = rng.random((B, Ld)) < 0.6
+    dv[:, 0] = True
+    rm, sc = oracle.maxsim(q, d, d_valid=dv)
+    # permuting the documents (with their mask) changes nothing
+    perm = rng.permutation(Ld)
+    rm2, sc2 = oracle.maxsim(q, d[:, perm], d_valid=dv[:, perm])
+    np.testing.assert_allclose(rm2, rm, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sc2, sc, rtol=0, atol=1e-13)
+    # an invalid document never wins, whatever it holds
+    d3 = d.copy()
+    d3[~dv] = 1e6
+    rm3, _ = oracle.maxsim(q, d3, d_valid=dv)
+    np.testing.assert_array_equal(rm3, rm)
+    # padding documents at the end equals dropping them
+    lens = np.array([3, 9])
+    dvp = np.arange(Ld)[None, :] < lens[:, None]
+    rmp, scp = oracle.maxsim(q, d, d_valid=dvp)
+    for b in range(B):
+        rmt, sct = oracle.maxsim(q[b:b + 1], d[b:b + 1, :lens[b]])
+        np.testing.assert_allclose(rmp[b], rmt[0], rtol=0, atol=1e-13)
+        assert abs(scp[b] - sct[0]) < 1e-13
+    # scaling the queries by c > 0 scales every max by c
+    rm4, sc4 = oracle.maxsim(2.5 * q, d, d_valid=dv)
+    np.testing.assert_allclose(rm4, 2.5 * rm, rtol=1e-13)
+
+
+def test_maxsim_against_torch_on_the_pages_shapes():
+    # the page's example sizes: 4 samples, 32 query and 256 document tokens, width 768,
+    # no masks; torch float64 matmul, max over documents, sum / L_q
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(4, 32, 768, generator=g, dtype=torch.float64)
+    d = torch.randn(4, 256, 768, generator=g, dtype=torch.float64)
+    sim = torch.matmul(q, d.transpose(1, 2))
+    want_rm = sim.max(dim=2).values
+    want = want_rm.sum(dim=1) / 32
+    rm, sc = oracle.maxsim(q, d)
+    np.testing.assert_allclose(rm, want_rm.numpy(), rtol=1e-13, atol=1e-12)
+    np.testing.assert_allclose(sc, want.numpy(), rtol=1e-13)
+
+
+def test_maxsim_query_mask_and_empty_cases():
+    rng = np.random.default_rng(7)
+    q, d = rng.standard_normal((2, 4, 3)), rng.standard_normal((2, 5, 3))
+    qv = np.array([[True, False, True, True], [False] * 4])
+    rm, sc = oracle.maxsim(q, d, q_valid=qv)
+    full, _ = oracle.maxsim(q, d)
+    assert rm[0, 1] == -np.inf and np.all(rm[1] == -np.inf)
+    assert abs(sc[0] - (full[0, 0] + full[0, 2] + full[0, 3]) / 4) < 1e-14
+    assert sc[1] == 0.0                                  # no valid query token
+    # no valid document: every valid query row is -inf, and so is the score
+    rm, sc = oracle.maxsim(q, d, d_valid=np.zeros((2, 5), dtype=bool))
+    assert np.all(rm == -np.inf) and np.all(sc == -np.inf)
+    rm, sc = oracle.maxsim(q, np.zeros((2, 0, 3)))
+    assert np.all(rm == -np.inf) and np.all(sc == -np.inf)
+    # no query tokens at all
+    rm, sc = oracle.maxsim(np.zeros((2, 0, 3)), d)
+    assert rm.shape == (2, 0) and np.all(sc == 0.0)

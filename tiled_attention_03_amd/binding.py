@@ -23,7 +23,7 @@ FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_EXPLICIT, FA_MASK_MODALITY, FA_MASK_PADDIN
 FA_PSE_NONE, FA_PSE_ALIBI, FA_PSE_DENSE = 0, 1, 2
 
 ENTRY_POINTS = ("fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep", "fa_bwd_main",
-                "fa_bwd_post", "fa_status_str", "fa_abi_version")
+                "fa_bwd_post", "fa_maxsim", "fa_status_str", "fa_abi_version")
 
 _DTYPES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _LAYOUTS = {"BNSD": FA_BNSD, "BSH": FA_BSH}
@@ -63,6 +63,20 @@ class FaProblem(ctypes.Structure):
     ]
 
 
+class FaMaxsimProblem(ctypes.Structure):
+    """Mirror of ``fa_maxsim_problem`` in include/fa.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("len_q", ctypes.c_int32),
+        ("len_d", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("pad0", ctypes.c_int32),
+        ("q_valid", ctypes.c_void_p),
+        ("d_valid", ctypes.c_void_p),
+    ]
+
+
 class FaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -84,6 +98,7 @@ def _load():
         "fa_bwd_prep": [P, vp, vp, vp, sz, vp],
         "fa_bwd_main": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "fa_bwd_post": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "fa_maxsim": [ctypes.POINTER(FaMaxsimProblem), vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -194,7 +209,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
         p.q_modality, p.k_modality = qm.data_ptr(), km.data_ptr()
         keep += [qm, km]
     if key_valid is not None:
-        kv = key_valid.to(torch.uint8).contiguous()
+        kv = _as_bytes(key_valid)
         if tuple(kv.shape) != (B, Sk):
             raise ValueError("key_valid must be [B, S_k]")
         flags |= FA_MASK_PADDING
@@ -224,6 +239,14 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
         p.pse_stride_q = ps.stride(2)
         keep.append(ps)
     return p, keep
+
+
+def _as_bytes(m: torch.Tensor) -> torch.Tensor:
+    """A mask as contiguous uint8 (0/1): bool storage is reinterpreted, not copied."""
+    m = m.contiguous()
+    if m.dtype == torch.bool:
+        return m.view(torch.uint8)
+    return m if m.dtype == torch.uint8 else (m != 0).view(torch.uint8)
 
 
 def _check(status: int, what: str):
@@ -313,3 +336,38 @@ def problem_kwargs(pr, device) -> dict:
                 modality_allow=pr.modality_allow, modality_allow_diag=pr.modality_allow_diag,
                 key_valid=mv(pr.key_valid), alibi_slopes=mv(pr.alibi_slopes), pse=mv(pr.pse),
                 keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed)
+
+
+def maxsim_problem(q: torch.Tensor, d: torch.Tensor, q_valid: Optional[torch.Tensor] = None,
+                   d_valid: Optional[torch.Tensor] = None):
+    """Build an ``FaMaxsimProblem`` (shape checks only) and the tensors it references."""
+    if q.dim() != 3 or d.dim() != 3 or q.shape[0] != d.shape[0] or q.shape[2] != d.shape[2]:
+        raise ValueError("q must be [B, L_q, D] and d [B, L_d, D]")
+    if q.dtype not in _DTYPES or d.dtype != q.dtype:
+        raise TypeError("q and d must share one dtype")
+    B, Lq, D = q.shape
+    Ld = d.shape[1]
+    p = FaMaxsimProblem()
+    p.batch, p.len_q, p.len_d, p.dim, p.dtype = B, Lq, Ld, D, _DTYPES[q.dtype]
+    keep = []
+    for name, m, L in (("q_valid", q_valid, Lq), ("d_valid", d_valid, Ld)):
+        if m is None:
+            continue
+        mm = _as_bytes(m)
+        if tuple(mm.shape) != (B, L):
+            raise ValueError(f"{name} must be [B, {L}]")
+        setattr(p, name, mm.data_ptr())
+        keep.append(mm)
+    return p, keep
+
+
+def maxsim(q, d, *, q_valid=None, d_valid=None, rowmax=None, score=None):
+    """MaxSim late interaction: (rowmax float32 [B, L_q], score float32 [B])."""
+    _contig(q, d)
+    p, keep = maxsim_problem(q, d, q_valid, d_valid)
+    B, Lq = q.shape[0], q.shape[1]
+    rm = torch.empty(B, Lq, dtype=torch.float32, device=q.device) if rowmax is None else rowmax
+    sc = torch.empty(B, dtype=torch.float32, device=q.device) if score is None else score
+    _check(lib.fa_maxsim(ctypes.byref(p), _ptr(q), _ptr(d), _ptr(rm), _ptr(sc), _stream()),
+           "fa_maxsim")
+    return rm, sc

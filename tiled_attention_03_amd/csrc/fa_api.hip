@@ -235,4 +235,29 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
   return fa_bwd_post(p, q, k, v, lse, dout, dq, workspace, workspace_bytes, stream);
 }
 
+fa_status fa_maxsim(const fa_maxsim_problem *p, const void *q, const void *d, float *rowmax,
+                    float *score, hipStream_t stream) {
+  if (!p) return FA_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->len_q < 0 || p->len_d < 0 || p->dim <= 0 || p->pad0 != 0)
+    return FA_ERR_INVALID_ARG;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (p->dim % 128 != 0 || p->dim > kMaxSimMaxDim || p->len_d > kMaxSimMaxDocs)
+    return FA_ERR_UNSUPPORTED;
+  const int64_t b_pad = ((int64_t)p->batch + 7) / 8 * 8;
+  if (b_pad * ((p->len_q + 31) / 32) > INT32_MAX || (int64_t)p->batch * p->len_q > INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
+  if (p->batch == 0) return FA_OK;
+  if (!score || ((uintptr_t)score & 3u)) return FA_ERR_INVALID_ARG;
+  if (p->len_q > 0 && (!tensor_ok(q) || !rowmax || ((uintptr_t)rowmax & 3u)))
+    return FA_ERR_INVALID_ARG;
+  if (p->len_q > 0 && p->len_d > 0 && !tensor_ok(d)) return FA_ERR_INVALID_ARG;
+  MaxSimParams r;
+  memset(&r, 0, sizeof(r));
+  r.q = q; r.d = d; r.q_valid = p->q_valid; r.d_valid = p->d_valid;
+  r.rowmax = rowmax; r.score = score;
+  r.B = p->batch; r.Lq = p->len_q; r.Ld = p->len_d; r.D = p->dim;
+  return hip_status(launch_maxsim(r, p->dtype, stream));
+}
+
 }  // extern "C"

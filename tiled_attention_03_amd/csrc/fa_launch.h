@@ -23,4 +23,16 @@ hipError_t launch_bwd_kv_f32(const Params &p, hipStream_t s);
 hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_bwd_q_f32(const Params &p, hipStream_t s);
 
+// MaxSim late-interaction scores (see fa_maxsim in include/fa.h).
+struct MaxSimParams {
+  const void *q, *d;               // [B, Lq, D], [B, Ld, D]
+  const uint8_t *q_valid, *d_valid;  // [B, Lq], [B, Ld] or null
+  float *rowmax;                   // [B, Lq]
+  float *score;                    // [B]
+  int B, Lq, Ld, D;
+};
+constexpr int kMaxSimMaxDim = 1024;     // D: multiple of 128, at most this
+constexpr int kMaxSimMaxDocs = 16384;   // L_d at most this
+hipError_t launch_maxsim(const MaxSimParams &p, int dtype, hipStream_t s);
+
 }  // namespace fa

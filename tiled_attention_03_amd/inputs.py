@@ -152,3 +152,40 @@ def config(cid: int, with_do: bool = True) -> Problem:
                        torch.bfloat16, 1.0 / math.sqrt(D), q, k, v, do, causal=True,
                        alibi_slopes=alibi_slopes(H))
     raise ValueError(f"unknown config {cid}")
+
+
+@dataclass
+class MaxSimCase:
+    """Operands of one MaxSim call: q [B, L_q, D], d [B, L_d, D] on the CPU."""
+    name: str
+    q: torch.Tensor
+    d: torch.Tensor
+    q_valid: Optional[torch.Tensor] = None     # bool [B, L_q]
+    d_valid: Optional[torch.Tensor] = None     # bool [B, L_d]
+
+
+def maxsim_workload() -> MaxSimCase:
+    """The late-interaction workload's own tensors as MaxSim operands: its
+    query and document embeddings (width 768) and its document padding."""
+    pr = config(4, with_do=False)
+    return MaxSimCase("maxsim_bf16_b256lq32ld512d768", pr.q, pr.k, None, pr.key_valid)
+
+
+def maxsim_case(B, Lq, Ld, D, dtype, seed, q_mask=None, d_mask=None) -> MaxSimCase:
+    """N(0,1) embeddings; masks: None, "pad" (valid prefix of random length) or
+    "holes" (each token valid with probability 0.8)."""
+    q = randn((B, Lq, D), dtype, seed)
+    d = randn((B, Ld, D), dtype, seed + 1)
+    g = _gen(seed + 2)
+
+    def mask(kind, L):
+        if kind is None:
+            return None
+        if kind == "pad":
+            lens = torch.randint(0, L + 1, (B,), generator=g)
+            return torch.arange(L)[None, :] < lens[:, None]
+        if kind == "holes":
+            return torch.rand(B, L, generator=g) < 0.8
+        raise ValueError(kind)
+
+    return MaxSimCase(f"maxsim_b{B}lq{Lq}ld{Ld}d{D}", q, d, mask(q_mask, Lq), mask(d_mask, Ld))
