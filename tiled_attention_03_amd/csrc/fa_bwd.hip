@@ -201,6 +201,24 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
           }
         }
       } else {
+        // dropout: the four lanes of a quad hold four consecutive keys and the
+        // same 16 queries, so lane q of the quad draws the Philox words of the
+        // queries with r % 4 == q (one call covers the quad's four keys), packs
+        // the keep bits, and the quad exchanges them
+        uint32_t kq[4] = {0u, 0u, 0u, 0u};
+        if (DROP) {
+          uint32_t mine = 0u;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            mine |= dropout_keep4(p, b, h, i0 + 8 * rr + 4 * g + (l & 3), my_j) << (4 * rr);
+          // quad_perm broadcasts of lane 0, 1, 2, 3
+          kq[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+          kq[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+          kq[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+          kq[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) kq[q] >>= (l & 3);
+        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x4 ls = *(const f32x4 *)&lse_s[cur][8 * rr + 4 * g];
@@ -211,15 +229,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
             const int i = i0 + 8 * rr + 4 * g + q;
             bool ok = i < p.Sq && my_j < p.Sk;
             if (ok) ok = allowed_elem(p, b, h, i, my_j);
-            float pr = 0.f, m = 1.f;
+            float pr = 0.f;
             if (ok) {
               float t = s[r] * c_log2;
               if (alibi) t -= sl2 * fabsf((float)(i - my_j));
               else if (dense) t += dense_bias(p, b, h, i, my_j) * kLog2e;
               pr = exp2_fast(t - ls[q]);
-              if (DROP) m = dropout_factor(p, b, h, i, my_j);
             }
             // dropout: P o M / keep_prob feeds dV, and dP is masked the same way
+            const float m = DROP ? dropout_scale(p, (kq[q] >> (4 * rr)) & 1u) : 1.f;
             s[r] = pr * m;
             dp[r] = pr * (dp[r] * m - dl[q]);
           }
@@ -553,19 +571,26 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
             dp[r] = pr * (dp[r] - dlt);
           }
         } else {
+          // keys 4t .. 4t + 3 of a register group share one Philox call
+          uint32_t keep[4] = {0u, 0u, 0u, 0u};
+          if (DROP) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              keep[rr] = dropout_keep4(p, b, h, my_i, k0 + 32 * jb + 8 * rr + 4 * g);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
             bool ok = j < p.Sk && my_i < p.Sq;
             if (ok) ok = allowed_elem(p, b, h, my_i, j);
-            float pr = 0.f, m = 1.f;
+            float pr = 0.f;
             if (ok) {
               float t = s[r] * c_log2;
               if (alibi) t -= sl2 * fabsf((float)(my_i - j));
               else if (dense) t += dense_bias(p, b, h, my_i, j) * kLog2e;
               pr = exp2_fast(t - lse2);
-              if (DROP) m = dropout_factor(p, b, h, my_i, j);
             }
+            const float m = DROP ? dropout_scale(p, (keep[r >> 2] >> (r & 3)) & 1u) : 1.f;
             dp[r] = pr * (dp[r] * m - dlt);   // dropout masks dP like P
           }
         }

@@ -65,41 +65,39 @@ struct Params {
 // numbers: as easy as 1, 2, 3", SC 2011): each round multiplies counter words
 // 0 and 2 by the round constants, and the new counter is (hi(w2*M1) ^ c1 ^ k0,
 // lo(w2*M1), hi(w0*M0) ^ c3 ^ k1, lo(w0*M0)); the key is bumped by the Weyl
-// constants between rounds.
+// constants between rounds.  Each product is one 32x32 -> 64-bit multiply
+// (v_mad_u64_u32) rather than separate high and low halves.
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
   constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
   constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(M0, c[0]), lo0 = M0 * c[0];
-    const uint32_t hi1 = __umulhi(M1, c[2]), lo1 = M1 * c[2];
-    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    const uint64_t p0 = (uint64_t)M0 * c[0];
+    const uint64_t p1 = (uint64_t)M1 * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
     c[0] = n0;
-    c[1] = lo1;
+    c[1] = (uint32_t)p1;
     c[2] = n2;
-    c[3] = lo0;
+    c[3] = (uint32_t)p0;
     k0 += W0;
     k1 += W1;
   }
 }
 
-// The dropout words of keys 4*(j/4) .. 4*(j/4) + 3 for query i of head (b, h):
-// the Philox output for counter (j/4, i, h, b); word j % 4 belongs to key j.
-__device__ __forceinline__ void dropout_words(const Params &p, int b, int h, int i, int j,
-                                              uint32_t (&w)[4]) {
-  w[0] = (uint32_t)(j >> 2);
-  w[1] = (uint32_t)i;
-  w[2] = (uint32_t)h;
-  w[3] = (uint32_t)b;
+// Keep bits of keys 4*(j/4) .. 4*(j/4) + 3 for query i of head (b, h): bit t
+// is set iff word t of the Philox output for counter (j/4, i, h, b), under
+// the seed as key, is below the threshold.  One call serves four keys.
+__device__ __forceinline__ uint32_t dropout_keep4(const Params &p, int b, int h, int i, int j) {
+  uint32_t w[4] = {(uint32_t)(j >> 2), (uint32_t)i, (uint32_t)h, (uint32_t)b};
   philox4x32_10(w, p.seed_lo, p.seed_hi);
+  return (uint32_t)(w[0] < p.drop_thr) | ((uint32_t)(w[1] < p.drop_thr) << 1) |
+         ((uint32_t)(w[2] < p.drop_thr) << 2) | ((uint32_t)(w[3] < p.drop_thr) << 3);
 }
 
-// Factor that multiplies probability (i, j) in P V and in dP: inv_keep if the
-// element is kept, else 0.
-__device__ __forceinline__ float dropout_factor(const Params &p, int b, int h, int i, int j) {
-  uint32_t w[4];
-  dropout_words(p, b, h, i, j, w);
-  return w[j & 3] < p.drop_thr ? p.inv_keep : 0.f;
+// The factor for keep bit `bit`: inv_keep if kept, else 0.
+__device__ __forceinline__ float dropout_scale(const Params &p, uint32_t bit) {
+  return bit ? p.inv_keep : 0.f;
 }
 
 // ------------------------------------------------------------------------

@@ -452,11 +452,11 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
           for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-              uint32_t wd[4];
-              dropout_words(p, b, h, my_i[rb], k0 + 32 * kb + 8 * rr + 4 * g, wd);
+              const uint32_t keep =
+                  dropout_keep4(p, b, h, my_i[rb], k0 + 32 * kb + 8 * rr + 4 * g);
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                s[rb][kb][4 * rr + q] *= wd[q] < p.drop_thr ? p.inv_keep : 0.f;
+                s[rb][kb][4 * rr + q] *= dropout_scale(p, (keep >> q) & 1u);
             }
         }
 #pragma unroll
