@@ -58,6 +58,21 @@
  * keep_prob)^T dO, dS = P o (M o (dO V^T) / keep_prob - delta) with
  * delta_i = sum_d dO_id O_id.  F16/BF16 only.
  *
+ * Gradient precision (page 1, tuning section: forward in 16 bits, backward in
+ * 32): with grad_f32 set, dQ, dK and dV are written as float32 (layout of
+ * Q/K/V, 16-byte aligned) instead of the input dtype.  They are the same
+ * float32 values the kernels would otherwise round to 16 bits: the products
+ * still take their operands (P, dS, inputs) in the input dtype with float32
+ * accumulation.  Ignored for FA_F32 inputs, whose gradients are float32.
+ *
+ * Bias gradient (a learnable dense pse): when dpse is non-null, fa_bwd /
+ * fa_bwd_main also write dpse[b, h, i, j] = dL/d(bias_ij) = dS_ij, the
+ * gradient of the softmax's input (with dropout, dS_ij = P_ij (Z_ij dP_ij -
+ * delta_i)); float32, contiguous [B, H, S_q, S_k], 16-byte aligned, every
+ * element written (0 where the mask hides the pair).  Only with
+ * pse_kind == FA_PSE_DENSE and F16/BF16 inputs; the dense bias may still be
+ * broadcast in the forward, the gradient is per (b, h).
+ *
  * Bias (pse, added after scaling, never scaled itself):
  *   FA_PSE_ALIBI  bias(h,i,j) = -alibi_slopes[h] * |i - j|, slopes float32 [H].
  *   FA_PSE_DENSE  bias element [b*pse_stride_b + h*pse_stride_h +
@@ -66,7 +81,8 @@
  * Errors: every check runs before any launch; a call that fails validation
  * writes nothing.  FA_ERR_INVALID_ARG: null pointer where one is needed,
  * negative sizes, H*D mismatch, M out of range, bad enum,
- * keep_prob outside (0, 1].  FA_ERR_UNSUPPORTED: keep_prob < 1 with F32, a
+ * keep_prob outside (0, 1], reserved0 != 0, dpse set without a dense pse or
+ * misaligned.  FA_ERR_UNSUPPORTED: keep_prob < 1 with F32, dpse with F32, a
  * head_dim the kernels do not cover (F16/BF16: 64 or 128; F32: 32, 64 or
  * 128).  FA_ERR_WORKSPACE: workspace
  * too small.  FA_ERR_HIP: a HIP launch reported an error.
@@ -89,7 +105,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_OK = 0,
@@ -136,6 +152,9 @@ typedef struct fa_problem {
   const void *pse;                   /* dense bias */
   int64_t pse_stride_b, pse_stride_h, pse_stride_q;
   uint64_t dropout_seed;             /* Philox key when keep_prob < 1 */
+  int32_t grad_f32;                  /* nonzero: the backward writes dQ, dK, dV as float32 */
+  int32_t reserved0;                 /* must be 0 */
+  float *dpse;                       /* optional backward output, see "Bias gradient" */
 } fa_problem;
 
 /* Forward: O (layout/dtype of Q) and LSE (float32 [B,H,S_q]). */

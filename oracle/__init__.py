@@ -272,19 +272,24 @@ def attention_fwd(q, k, v, scale, keep_prob=1.0, dropout_seed=0, **masks):
     return O, LSE
 
 
-def attention_bwd(q, k, v, do, scale, keep_prob=1.0, dropout_seed=0, **masks):
+def attention_bwd(q, k, v, do, scale, keep_prob=1.0, dropout_seed=0, return_dbias=False,
+                  **masks):
     """dQ, dK, dV (float64, BNSD) of L = sum(O * dO).
 
     With P the forward probabilities and Z the dropout factors (1 without
     dropout): dV_j = sum_i P_ij Z_ij dO_i;  dP_ij = Z_ij dO_i . v_j;
     D_i = sum_j P_ij dP_ij;  dS_ij = P_ij (dP_ij - D_i);
     dQ_i = scale sum_j dS_ij k_j;  dK_j = scale sum_i dS_ij q_i.
-    The bias has no parameters here."""
+    dS is the gradient of L with respect to the softmax's input, hence also
+    with respect to an additive bias element; ``return_dbias`` appends it as
+    a fourth result, float64 [B, H, Sq, Sk] (one slice per (b, h), before
+    any reduction over a broadcast bias)."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     mk = _masks(masks)
     B, H, Sq = q.shape[:3]
     Sk = k.shape[2]
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dbias = np.zeros((B, H, Sq, Sk)) if return_dbias else None
     for b in range(B):
         for h in range(H):
             P, _ = softmax_rows(head_scores(q, k, scale, b, h, mk))
@@ -297,7 +302,9 @@ def attention_bwd(q, k, v, do, scale, keep_prob=1.0, dropout_seed=0, **masks):
             dS = P * (dP - Dl[:, None])
             dq[b, h] = scale * (dS @ k[b, h])
             dk[b, h] = scale * (dS.T @ q[b, h])
-    return dq, dk, dv
+            if dbias is not None:
+                dbias[b, h] = dS
+    return (dq, dk, dv) if dbias is None else (dq, dk, dv, dbias)
 
 
 def problem_masks(p) -> dict:
@@ -325,12 +332,13 @@ def problem_fwd(p):
     return (bnsd_to_bsh(O) if p.layout == "BSH" else O), LSE
 
 
-def problem_bwd(p):
+def problem_bwd(p, return_dbias=False):
     """(dQ, dK, dV) for a problem with upstream gradient ``p.do``, each in the
-    problem's own layout (float64)."""
+    problem's own layout (float64); with ``return_dbias`` also dS [B,H,Sq,Sk]."""
     g = attention_bwd(_bnsd(p.q, p), _bnsd(p.k, p), _bnsd(p.v, p), _bnsd(p.do, p), p.scale,
-                      **_problem_drop(p), **problem_masks(p))
-    return tuple(bnsd_to_bsh(x) if p.layout == "BSH" else x for x in g)
+                      return_dbias=return_dbias, **_problem_drop(p), **problem_masks(p))
+    out = tuple(bnsd_to_bsh(x) if p.layout == "BSH" else x for x in g[:3])
+    return out + (g[3],) if return_dbias else out
 
 
 def maxsim(q, d, q_valid=None, d_valid=None):

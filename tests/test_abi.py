@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.abi_version() == 3
+    assert fa.abi_version() == 4
     assert fa.status_str(0) == "ok"
     assert fa.status_str(-2) == "unsupported configuration"
 
@@ -97,6 +97,11 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
     ({"pse_kind": fa.FA_PSE_DENSE}, fa.FA_ERR_INVALID_ARG),
     ({"pse_kind": 5}, fa.FA_ERR_INVALID_ARG),
     ({"scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
+    ({"reserved0": 1}, fa.FA_ERR_INVALID_ARG),
+    ({"dpse": 1 << 20}, fa.FA_ERR_INVALID_ARG),                       # no dense pse
+    ({"dpse": (1 << 20) + 4, "pse_kind": fa.FA_PSE_DENSE, "pse": 1 << 20}, fa.FA_ERR_INVALID_ARG),
+    ({"dpse": 1 << 20, "pse_kind": fa.FA_PSE_DENSE, "pse": 1 << 20, "dtype": fa.FA_F32},
+     fa.FA_ERR_UNSUPPORTED),
 ])
 def test_validation_codes(over, code):
     assert call_fwd(base_problem(**over)) == code

@@ -305,3 +305,95 @@ def test_dropout_seed_changes_the_mask_and_repeats():
     pr.dropout_seed = 6
     o3, _ = gpu_fwd(pr)
     assert not torch.equal(o1, o3)
+
+
+# ----------------------------------------------------------------------------------
+# float32 gradient outputs and the bias gradient
+
+GRADF32 = []
+_gseed = 2000
+for D in (64, 128):
+    for dtype in (torch.bfloat16, torch.float16):
+        for mask, kp in (("none", 1.0), ("causal+alibi", 1.0), ("padding", 1.0), ("dense", 1.0),
+                         ("causal", 0.8)):
+            GRADF32.append((2, 2, 200, 333, D, dtype, "BNSD", mask, kp, _gseed))
+            _gseed += 1
+GRADF32.append((2, 2, 160, 96, 128, torch.bfloat16, "BSH", "modality+holes+causal", 1.0, _gseed))
+GRADF32.append((1, 4, 1024, 1024, 128, torch.bfloat16, "BNSD", "causal+alibi", 1.0, _gseed + 1))
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,kp,seed", GRADF32,
+                         ids=[f"{c[5]}-D{c[4]}-{c[6]}-{c[2]}x{c[3]}-{c[7]}-kp{c[8]}"
+                              .replace("torch.", "") for c in GRADF32])
+def test_float32_gradients(B, H, Sq, Sk, D, dtype, layout, mask, kp, seed):
+    """grad_f32 writes the kernels' own float32 values: rounded to the input dtype
+    they are bit-identical to the 16-bit outputs, and they meet the parity bar."""
+    pr = make_case(B, H, Sq, Sk, D, dtype, layout, mask, seed)
+    pr.keep_prob, pr.dropout_seed = kp, seed
+    o, lse = gpu_fwd(pr)
+    g16 = gpu_bwd(pr, o, lse)
+    pr.grad_f32 = True
+    g32 = gpu_bwd(pr, o, lse)
+    ref = oracle.problem_bwd(pr)
+    for name, a, b, r in zip(("dQ", "dK", "dV"), g16, g32, ref):
+        assert b.dtype == torch.float32 and a.dtype == dtype
+        # rounding the float32 value gives the 16-bit one, except at an exact tie between two
+        # 16-bit neighbours: the fp16 key pass forms dK = acc * scale and its rounding in one
+        # fused step (v_fma_mixlo_f16), i.e. from the exact product, not its float32 rounding
+        rb = b.to(dtype)
+        bad = rb != a
+        if bad.any():
+            bf, af, rf = b[bad].double(), a[bad].double(), rb[bad].double()
+            assert torch.all((bf - af).abs() == (bf - rf).abs()), \
+                f"{name}: float32 output does not round to the 16-bit one"
+            print(f"  {name}: {int(bad.sum())} exact ties rounded the other way")
+        assert_close(name, b, r, dtype, grow=1.0 / kp)
+
+
+DPSE = [
+    (2, 3, 97, 150, 64, torch.bfloat16, "BNSD", "dense", 1.0, 2100),
+    (2, 2, 130, 130, 128, torch.bfloat16, "BNSD", "dense+causal", 1.0, 2101),
+    (1, 2, 70, 300, 128, torch.float16, "BNSD", "dense+padding", 1.0, 2102),
+    (2, 2, 160, 96, 128, torch.bfloat16, "BSH", "dense+causal", 0.75, 2103),
+    (1, 2, 33, 65, 64, torch.bfloat16, "BNSD", "dense+explicit", 1.0, 2104),
+]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,kp,seed", DPSE,
+                         ids=[f"{c[7]}-{c[6]}-{c[2]}x{c[3]}-kp{c[8]}" for c in DPSE])
+def test_bias_gradient(B, H, Sq, Sk, D, dtype, layout, mask, kp, seed):
+    pr = make_case(B, H, Sq, Sk, D, dtype, layout, mask, seed)
+    pr.keep_prob, pr.dropout_seed = kp, seed
+    o, lse = gpu_fwd(pr)
+    q, k, v, do = (t.to(DEV) for t in (pr.q, pr.k, pr.v, pr.do))
+    dpse = torch.full((B, H, Sq, Sk), float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv, dp = fa.bwd(q, k, v, o, lse, do, heads=pr.heads, layout=pr.layout, dpse=dpse,
+                            **fa.problem_kwargs(pr, DEV))
+    torch.cuda.synchronize()
+    rq, rk, rv, rds = oracle.problem_bwd(pr, return_dbias=True)
+    assert torch.isfinite(dp).all(), "bias gradient elements left unwritten"
+    # dS_ij = P_ij (dP_ij - D_i) with D_i = dO_i . O_i read from O rounded to the input
+    # dtype: besides the stated bar, dS may carry P_ij * u * sum_d |dO_id O_id| (u = 2^-8,
+    # the unit roundoff of bf16 and fp16), which no sum over i or j averages away here
+    P = np.stack([np.stack([oracle.probabilities(
+        oracle.bsh_to_bnsd(pr.q.double().numpy(), H) if layout == "BSH" else pr.q,
+        oracle.bsh_to_bnsd(pr.k.double().numpy(), H) if layout == "BSH" else pr.k,
+        pr.scale, bb, hh, **oracle.problem_masks(pr)) for hh in range(H)]) for bb in range(B)])
+    O_ref, _ = oracle.problem_fwd(pr)
+    dO = pr.do.double().numpy()
+    if layout == "BSH":
+        O_ref, dO = oracle.bsh_to_bnsd(O_ref, H), oracle.bsh_to_bnsd(dO, H)
+    rowterm = (np.abs(dO) * np.abs(O_ref)).sum(axis=-1)          # [B, H, Sq]
+    extra = P * (2.0 ** -8 * rowterm)[..., None]
+    e = np.abs(dp.cpu().double().numpy() - rds)
+    tmax, tmean = (t / kp for t in (2e-2 if dtype == torch.bfloat16 else 5e-3,
+                                     2e-3 if dtype == torch.bfloat16 else 5e-4))
+    print(f"  dpse: max-abs {e.max():.3e}, worst / bar "
+          f"{(e / (tmax + extra)).max():.3f}, mean-abs {e.mean():.3e}")
+    assert np.all(e <= tmax + extra) and e.mean() <= tmean
+    if "causal" in mask:
+        assert torch.all(dp.triu(1) == 0)
+    # the other gradients are unchanged by asking for the bias gradient
+    g = gpu_bwd(pr, o, lse)
+    for a, b in zip((dq, dk, dv), g):
+        assert torch.equal(a, b)

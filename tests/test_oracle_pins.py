@@ -696,3 +696,35 @@ def test_maxsim_query_mask_and_empty_cases():
     # no query tokens at all
     rm, sc = oracle.maxsim(np.zeros((2, 0, 3)), d)
     assert rm.shape == (2, 0) and np.all(sc == 0.0)
+
+
+# ----------------------------------------------------------------------------------
+# the bias gradient dS (a learnable dense pse)
+
+@pytest.mark.parametrize("extra", [dict(), dict(causal=True), dict(keep_prob=0.7, dropout_seed=9)],
+                         ids=["dense", "dense_causal", "dense_dropout"])
+def test_bias_gradient_central_differences(extra):
+    B, H, Sq, Sk, D = 1, 2, 4, 5, 3
+    q, k, v, do = rnd((B, H, Sq, D), 191), rnd((B, H, Sk, D), 192), rnd((B, H, Sk, D), 193), \
+        rnd((B, H, Sq, D), 194)
+    pse = rnd((B, H, Sq, Sk), 195)
+    scale = 0.6
+
+    def loss(ps):
+        O, _ = oracle.attention_fwd(q, k, v, scale, pse=ps, **extra)
+        return float((O * do).sum())
+
+    *_, dbias = oracle.attention_bwd(q, k, v, do, scale, pse=pse, return_dbias=True, **extra)
+    eps = 1e-6
+    it = np.nditer(pse, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        plus, minus = pse.copy(), pse.copy()
+        plus[idx] += eps
+        minus[idx] -= eps
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        assert abs(fd - dbias[idx]) <= 1e-7 * max(1.0, abs(fd)), (idx, fd, dbias[idx])
+    # rows of dS sum to zero (adding a constant to a row's bias changes nothing)
+    np.testing.assert_allclose(dbias.sum(axis=3), 0, atol=1e-12)
+    if extra.get("causal"):
+        assert np.all(dbias[..., np.triu_indices(Sq, 1, Sk)[0], np.triu_indices(Sq, 1, Sk)[1]] == 0)

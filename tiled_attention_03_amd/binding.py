@@ -60,6 +60,9 @@ class FaProblem(ctypes.Structure):
         ("pse_stride_h", ctypes.c_int64),
         ("pse_stride_q", ctypes.c_int64),
         ("dropout_seed", ctypes.c_uint64),
+        ("grad_f32", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("dpse", ctypes.c_void_p),
     ]
 
 
@@ -139,7 +142,8 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
                  modality_allow_diag: bool = False,
                  key_valid: Optional[torch.Tensor] = None,
                  alibi_slopes: Optional[torch.Tensor] = None,
-                 pse: Optional[torch.Tensor] = None, dropout_seed: int = 0):
+                 pse: Optional[torch.Tensor] = None, dropout_seed: int = 0,
+                 grad_f32: bool = False, dpse: Optional[torch.Tensor] = None):
     """Build an ``FaProblem`` from tensors (shape checks only).  Returns the
     struct and the list of tensors whose memory it references."""
     if layout not in _LAYOUTS:
@@ -170,6 +174,12 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
     p.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     p.keep_prob = float(keep_prob)
     p.dropout_seed = int(dropout_seed) & 0xFFFFFFFFFFFFFFFF
+    p.grad_f32 = int(bool(grad_f32))
+    if dpse is not None:
+        if dpse.dtype != torch.float32 or tuple(dpse.shape) != (B, H, Sq, Sk) or \
+                not dpse.is_contiguous():
+            raise ValueError("dpse must be a contiguous float32 [B, H, S_q, S_k]")
+        p.dpse = dpse.data_ptr()
     keep = []
     flags = 0
     if causal:
@@ -285,18 +295,27 @@ def workspace_size(q, k, *, heads: int, layout: str = "BNSD", **kw) -> int:
     return n.value
 
 
-def bwd(q, k, v, o, lse, do, *, heads: int, layout: str = "BNSD", workspace=None, **kw):
-    """dQ, dK, dV of L = sum(O * dO), recomputing P from ``lse``."""
+def bwd(q, k, v, o, lse, do, *, heads: int, layout: str = "BNSD", workspace=None,
+        want_dpse: bool = False, dpse: Optional[torch.Tensor] = None, **kw):
+    """dQ, dK, dV of L = sum(O * dO), recomputing P from ``lse``.  With
+    ``grad_f32=True`` they are float32.  With ``want_dpse`` (or a ``dpse``
+    buffer, float32 [B, H, S_q, S_k]) the bias gradient is written and
+    returned as a fourth value."""
     _contig(q, k, v, o, lse, do)
-    p, keep = make_problem(q, k, heads=heads, layout=layout, **kw)
+    if want_dpse and dpse is None:
+        B = q.shape[0]
+        Sq, Sk = (q.shape[2], k.shape[2]) if layout == "BNSD" else (q.shape[1], k.shape[1])
+        dpse = torch.empty(B, heads, Sq, Sk, dtype=torch.float32, device=q.device)
+    p, keep = make_problem(q, k, heads=heads, layout=layout, dpse=dpse, **kw)
     n = ctypes.c_size_t(0)
     _check(lib.fa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)), "fa_bwd_workspace_size")
     ws = workspace if workspace is not None else torch.empty(max(n.value, 256), dtype=torch.uint8,
                                                              device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gdt = torch.float32 if p.grad_f32 else q.dtype
+    dq, dk, dv = (torch.empty(t.shape, dtype=gdt, device=t.device) for t in (q, k, v))
     _check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()), "fa_bwd")
-    return dq, dk, dv
+    return (dq, dk, dv) if dpse is None else (dq, dk, dv, dpse)
 
 
 class Plan:
@@ -335,7 +354,7 @@ def problem_kwargs(pr, device) -> dict:
                 q_modality=mv(pr.q_modality), k_modality=mv(pr.k_modality),
                 modality_allow=pr.modality_allow, modality_allow_diag=pr.modality_allow_diag,
                 key_valid=mv(pr.key_valid), alibi_slopes=mv(pr.alibi_slopes), pse=mv(pr.pse),
-                keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed)
+                keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed, grad_f32=pr.grad_f32)
 
 
 def maxsim_problem(q: torch.Tensor, d: torch.Tensor, q_valid: Optional[torch.Tensor] = None,

@@ -34,6 +34,11 @@ fa_status check_problem(const fa_problem *p) {
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
   if (!(p->keep_prob > 0.f && p->keep_prob <= 1.f)) return FA_ERR_INVALID_ARG;   // NaN too
   if (p->keep_prob < 1.f && p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (p->reserved0 != 0) return FA_ERR_INVALID_ARG;
+  if (p->dpse) {
+    if (p->pse_kind != FA_PSE_DENSE || !aligned16(p->dpse)) return FA_ERR_INVALID_ARG;
+    if (p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  }
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
   const uint32_t known = FA_MASK_CAUSAL | FA_MASK_EXPLICIT | FA_MASK_MODALITY | FA_MASK_PADDING;
   if (p->mask_flags & ~known) return FA_ERR_INVALID_ARG;
@@ -113,6 +118,8 @@ Params make_params(const fa_problem *p) {
   r.alibi_slopes = p->alibi_slopes;
   r.pse = p->pse;
   r.pse_sb = p->pse_stride_b; r.pse_sh = p->pse_stride_h; r.pse_sq = p->pse_stride_q;
+  r.grad_f32 = p->grad_f32 != 0 && p->dtype != FA_F32;
+  r.dpse = p->dpse;
   if (p->keep_prob < 1.f) {
     // keep iff word < floor(keep_prob * 2^32); keep_prob * 2^32 is exact in double
     r.dropout = 1;

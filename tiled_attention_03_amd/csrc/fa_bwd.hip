@@ -31,6 +31,8 @@
 // n+1 are loaded from global memory straight into LDS (no register staging)
 // while step n is multiplied, with one barrier per step; blocks the mask hides
 // entirely are skipped.
+#include <algorithm>
+
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -46,8 +48,9 @@ constexpr int KBQ = 64;     // keys per step, query pass
 // ===========================================================================
 // key pass: dK, dV
 // DROP: dropout compiled in (keep_prob < 1); the kernel without it carries no
-// dropout code at all.
-template <typename T, int D, bool DROP>
+// dropout code at all.  EXTRA: the optional outputs (float32 gradients, the
+// bias gradient) compiled in; likewise absent from the plain instance.
+template <typename T, int D, bool DROP, bool EXTRA>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
@@ -242,6 +245,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
             dp[r] = pr * (dp[r] * m - dl[q]);
           }
         }
+        if (EXTRA && p.dpse) {
+          // bias gradient: dS itself, before it is rounded for the products
+          float *dst = p.dpse + ((int64_t)(b * p.H + h) * p.Sq) * p.Sk + my_j;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (i < p.Sq && my_j < p.Sk) dst[(int64_t)i * p.Sk] = dp[r];
+          }
+        }
       }
       // dV += P^T dO, dK += dS^T Q, contraction over the 32 queries
 #pragma unroll
@@ -429,6 +441,22 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   }
 
   // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
+  if (EXTRA && p.grad_f32) {
+    float *DKg = (float *)p.dk + koff;
+    float *DVg = (float *)p.dv + koff;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jw + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (j < p.Sk) {
+          DKg[(int64_t)j * p.k_ss + 32 * db + lr] = dk[db][r] * p.scale;
+          DVg[(int64_t)j * p.k_ss + 32 * db + lr] = dv[db][r];
+        }
+      }
+    }
+    return;
+  }
   T *DKg = (T *)p.dk + koff;
   T *DVg = (T *)p.dv + koff;
 #pragma unroll
@@ -446,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 
 // ===========================================================================
 // query pass: dQ
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool EXTRA>
 __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
   constexpr int ES = (int)sizeof(T);
@@ -611,7 +639,20 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   }
 
   // dQ = scale * acc; element (db, r): column 32db + 8(r/4) + 4g + r%4
-  if (my_i < p.Sq) {
+  if (EXTRA && my_i < p.Sq && p.grad_f32) {
+    float *Dg = (float *)p.dq + qoff + (int64_t)my_i * p.q_ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * rr + e] * p.scale;
+        *(f32x4 *)(Dg + d0) = v;
+      }
+    }
+  } else if (my_i < p.Sq) {
     T *Dg = (T *)p.dq + qoff + (int64_t)my_i * p.q_ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -627,17 +668,37 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   }
 }
 
+// Zeros n floats (16-byte aligned): the bias gradient of pairs the key pass
+// never visits.  A kernel rather than a memset, so the call stays safe to
+// capture in a graph.
+__global__ __launch_bounds__(256) void zero_f32_kernel(float *dst, int64_t n) {
+  const int64_t n4 = n >> 2;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n4; k += (int64_t)gridDim.x * 256)
+    ((f32x4 *)dst)[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) dst[4 * n4 + threadIdx.x] = 0.f;
+}
+
 template <typename T, int D>
 hipError_t launch_kv(const Params &p, hipStream_t s) {
   const int n_ktiles = (p.Sk + KB - 1) / KB;
   const int64_t blocks = (int64_t)n_ktiles * p.B * p.H;
-  if (blocks == 0) return hipSuccess;
-  if (p.dropout)
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, true>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
-                       p, n_ktiles);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, false>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
-                       p, n_ktiles);
+  if (p.dpse) {
+    const int64_t n = (int64_t)p.B * p.H * p.Sq * p.Sk;
+    if (n > 0) {
+      const int64_t grid = std::min<int64_t>((n / 4 + 255) / 256 + 1, 4096);
+      hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, p.dpse, n);
+    }
+  }
+  if (blocks == 0) return hipGetLastError();
+  const bool extra = p.grad_f32 || p.dpse;
+  const dim3 grid((unsigned)blocks), block(NWB * 64);
+  if (p.dropout) {
+    if (extra) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true>), grid, block, 0, s, p, n_ktiles);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false>), grid, block, 0, s, p, n_ktiles);
+  } else {
+    if (extra) hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, true>), grid, block, 0, s, p, n_ktiles);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, false>), grid, block, 0, s, p, n_ktiles);
+  }
   return hipGetLastError();
 }
 
@@ -646,12 +707,15 @@ hipError_t launch_q(const Params &p, hipStream_t s) {
   const int n_qtiles = (p.Sq + QBQ - 1) / QBQ;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  if (p.dropout)
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, true>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
-                       p, n_qtiles);
-  else
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, false>), dim3((unsigned)blocks), dim3(NWB * 64), 0, s,
-                       p, n_qtiles);
+  const bool extra = p.grad_f32 != 0;
+  const dim3 grid((unsigned)blocks), block(NWB * 64);
+  if (p.dropout) {
+    if (extra) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true>), grid, block, 0, s, p, n_qtiles);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false>), grid, block, 0, s, p, n_qtiles);
+  } else {
+    if (extra) hipLaunchKernelGGL((bwd_q_kernel<T, D, false, true>), grid, block, 0, s, p, n_qtiles);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, false, false>), grid, block, 0, s, p, n_qtiles);
+  }
   return hipGetLastError();
 }
 

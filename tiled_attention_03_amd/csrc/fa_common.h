@@ -59,6 +59,10 @@ struct Params {
   uint32_t drop_thr;
   uint32_t seed_lo, seed_hi;
   float inv_keep;
+  // gradient outputs: float32 instead of the input dtype
+  int grad_f32;
+  // optional bias gradient, float32 contiguous [B, H, Sq, Sk]
+  float *dpse;
 };
 
 // Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random

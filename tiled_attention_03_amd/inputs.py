@@ -93,6 +93,7 @@ class Problem:
     pse: Optional[torch.Tensor] = None                # float32, broadcastable to [B,H,Sq,Sk]
     keep_prob: float = 1.0                            # < 1: dropout after the softmax
     dropout_seed: int = 0                             # Philox key of the dropout mask
+    grad_f32: bool = False                            # backward writes float32 gradients
     meta: dict = field(default_factory=dict)
 
 
