@@ -133,6 +133,70 @@ def maxsim_bytes(case) -> int:
     return B * Lq * D * es + valid_docs * D * es + mask + B * Lq * 4 + B * 4
 
 
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA: twice the bf16 rate
+
+
+def bench_fp8(args):
+    """The fp8 forward (pre-pass + main kernel) on the long workload's inputs,
+    quantized per tensor to e4m3.  Forward only: the fp8 path has no backward."""
+    import torch
+    from tiled_attention_03_amd import binding as fa
+    from tiled_attention_03_amd import inputs
+
+    pr = inputs.config(args.config, with_do=False)
+    dev = "cuda:0"
+    (q8, qs), (k8, ks), (v8, vs) = (inputs.fp8_quantize(t) for t in (pr.q, pr.k, pr.v))
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    kw = fa.problem_kwargs(pr, dev)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(pr.batch, pr.heads, pr.seq_q, dtype=torch.float32, device=dev)
+    p, keep = fa.make_problem(q8, k8, heads=pr.heads, layout=pr.layout, **kw)
+    import ctypes
+    n = ctypes.c_size_t(0)
+    fa._check(fa.lib.fa_fwd_fp8_workspace_size(ctypes.byref(p), ctypes.byref(n)), "workspace")
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    pp = ctypes.byref(p)
+    stream = fa._stream()
+
+    def call():
+        fa._check(fa.lib.fa_fwd_fp8(pp, fa._ptr(q8), fa._ptr(k8), fa._ptr(v8), qs, ks, vs,
+                                    fa._ptr(o), fa._ptr(lse), fa._ptr(ws), ws.numel(), stream),
+                  "fa_fwd_fp8")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    pairs = visible_pairs(pr)
+    flops = 4 * pr.head_dim * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s with fp8 (e4m3) inputs on 1 MI355X and % of fp8 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": pr.name, "batch": pr.batch, "heads": pr.heads, "seq_q": pr.seq_q,
+                   "seq_k": pr.seq_k, "head_dim": pr.head_dim, "layout": pr.layout,
+                   "causal": pr.causal, "pse": "alibi" if pr.alibi_slopes is not None else None,
+                   "pass": "fwd", "visible_pairs": pairs, "output": "bf16"},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"kernel": "fwd_fp8 (pre-pass + main)", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_maxsim(args):
     """The MaxSim kernel on the late-interaction workload's own tensors."""
     import torch
@@ -207,9 +271,9 @@ def main():
     ap.add_argument("--keep-prob", type=float, default=1.0,
                     help="dropout keep probability (1.0 = no dropout, the headline workload)")
     ap.add_argument("--dropout-seed", type=int, default=0x5EED)
-    ap.add_argument("--workload", choices=("attention", "maxsim"), default="attention",
+    ap.add_argument("--workload", choices=("attention", "maxsim", "fp8"), default="attention",
                     help="attention: the fused attention step (the headline); maxsim: the "
-                         "late-interaction MaxSim kernel")
+                         "late-interaction MaxSim kernel; fp8: the forward with e4m3 inputs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -232,6 +296,9 @@ def main():
 
     if args.workload == "maxsim":
         bench_maxsim(args)
+        return
+    if args.workload == "fp8":
+        bench_fp8(args)
         return
 
     import torch

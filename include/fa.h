@@ -105,7 +105,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_OK = 0,
@@ -115,7 +115,7 @@ typedef enum {
   FA_ERR_WORKSPACE = -4
 } fa_status;
 
-typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2, FA_FP8_E4M3 = 3 } fa_dtype;
 typedef enum { FA_BNSD = 0, FA_BSH = 1 } fa_layout;
 enum {
   FA_MASK_NONE = 0,
@@ -160,6 +160,22 @@ typedef struct fa_problem {
 /* Forward: O (layout/dtype of Q) and LSE (float32 [B,H,S_q]). */
 fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *v,
                  void *o, float *lse, hipStream_t stream);
+
+/* Forward with fp8 inputs (page 1, tuning section: pure fp8, experimental).
+ * p->dtype must be FA_FP8_E4M3: q, k, v hold OCP e4m3 bytes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; the value of a
+ * byte times its tensor's descale factor is the real input).  O is bf16 in
+ * Q's layout, LSE float32 [B,H,S_q], both as for fa_fwd, for the real inputs.
+ * Masks and bias as for fa_fwd; D = 64 or 128; keep_prob must be 1.
+ * The probabilities that multiply V are rounded to e4m3 (p = exp2 of the
+ * logit minus a running reference, at most 2^8); the row sums use them
+ * unrounded.  The workspace (fa_fwd_fp8_workspace_size bytes, 16-byte
+ * aligned) receives V transposed per 64-key tile; it needs no clearing.
+ * fa_fwd, fa_bwd* reject FA_FP8_E4M3 with FA_ERR_UNSUPPORTED. */
+fa_status fa_fwd_fp8_workspace_size(const fa_problem *p, size_t *bytes);
+fa_status fa_fwd_fp8(const fa_problem *p, const void *q, const void *k, const void *v,
+                     float q_descale, float k_descale, float v_descale, void *o, float *lse,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace fa_bwd needs: the float32 row terms
  * D_i = sum_d dO_id * O_id, [B,H,S_q], rounded up to 256 bytes. */

@@ -59,6 +59,7 @@ __all__ = [
     "bsh_to_bnsd", "bnsd_to_bsh", "allowed", "bias", "head_scores",
     "softmax_rows", "attention_fwd", "attention_bwd", "probabilities",
     "problem_masks", "problem_fwd", "problem_bwd", "philox4x32_10", "dropout_mask", "maxsim",
+    "e4m3_decode",
 ]
 
 
@@ -365,3 +366,17 @@ def maxsim(q, d, q_valid=None, d_valid=None):
         if Lq > 0:
             score[b] = rm[qv[b]].sum() / Lq
     return rowmax, score
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of OCP FP8 E4M3 bytes (the "fn" variant): bit 7 sign,
+    bits 6..3 exponent with bias 7, bits 2..0 mantissa; exponent 0 is
+    subnormal (m / 8 * 2^-6); 0x7f and 0xff are NaN; there are no infinities,
+    so exponent 15 with mantissa < 7 is a normal number (up to 448)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * val
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)

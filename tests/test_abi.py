@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.abi_version() == 4
+    assert fa.abi_version() == 5
     assert fa.status_str(0) == "ok"
     assert fa.status_str(-2) == "unsupported configuration"
 
@@ -182,3 +182,28 @@ def test_maxsim_pointer_checks():
     assert fa.lib.fa_maxsim(None, FAKE, FAKE, FAKE, FAKE, None) == fa.FA_ERR_INVALID_ARG
     # B == 0 is a no-op that needs no pointers
     assert call_maxsim(maxsim_problem(batch=0), q=None, d=None, rowmax=None, score=None) == 0
+
+
+def call_fwd_fp8(p, ws=FAKE, ws_bytes=1 << 30, scales=(1.0, 1.0, 1.0)):
+    return fa.lib.fa_fwd_fp8(ctypes.byref(p), FAKE, FAKE, FAKE, *scales, FAKE, FAKE, ws, ws_bytes,
+                             None)
+
+
+def test_fp8_entry_points_validate():
+    p8 = base_problem(dtype=fa.FA_FP8_E4M3, head_dim=128)
+    # the 16-bit entry points refuse fp8 problems, and the fp8 one refuses the others
+    assert call_fwd(p8) == fa.FA_ERR_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert fa.lib.fa_bwd_workspace_size(ctypes.byref(p8), ctypes.byref(n)) == fa.FA_ERR_UNSUPPORTED
+    assert call_fwd_fp8(base_problem()) == fa.FA_ERR_INVALID_ARG
+    # workspace: V^T per 64-key tile, B * H * ceil(S_k / 64) * D * 64 bytes
+    assert fa.lib.fa_fwd_fp8_workspace_size(ctypes.byref(p8), ctypes.byref(n)) == 0
+    assert n.value == 2 * 4 * 1 * 128 * 64
+    assert call_fwd_fp8(p8, ws_bytes=n.value - 1) == fa.FA_ERR_WORKSPACE
+    assert call_fwd_fp8(p8, ws=None, ws_bytes=n.value) == fa.FA_ERR_INVALID_ARG
+    assert call_fwd_fp8(p8, scales=(1.0, float("inf"), 1.0)) == fa.FA_ERR_INVALID_ARG
+    assert call_fwd_fp8(base_problem(dtype=fa.FA_FP8_E4M3, keep_prob=0.9)) == fa.FA_ERR_UNSUPPORTED
+    assert call_fwd_fp8(base_problem(dtype=fa.FA_FP8_E4M3, head_dim=96)) == fa.FA_ERR_UNSUPPORTED
+    # empty problems need nothing
+    assert fa.lib.fa_fwd_fp8(ctypes.byref(base_problem(dtype=fa.FA_FP8_E4M3, batch=0)), None, None,
+                             None, 1.0, 1.0, 1.0, None, None, None, 0, None) == 0

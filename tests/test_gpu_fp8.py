@@ -1,0 +1,148 @@
+"""GPU parity of the fp8 forward (fa_fwd_fp8 through the C ABI) against the
+fp64 oracle run on the exact real inputs the fp8 tensors stand for
+(e4m3 value times descale, decoded by the oracle's own e4m3 rule).
+
+Bar, derived per element from the kernel's arithmetic (no page states one for
+fp8): the kernel rounds each p = exp2(logit - reference) <= 2^8 to e4m3, with
+error <= 2^-4 p + 2^-10 in units where the row's largest p is >= 1, so in
+normalised terms |dO_id| <= sum_j (2^-4 P_ij + 2^-10 max_j P_ij) |v_jd| over
+the visible keys; O is then rounded to bf16 (<= 2^-8 |O_id|); the scores carry
+the float32 summation error of D exact products, |dt_ij| <= 2 D 2^-24
+sum_d |q_id k_jd| * c (c the base-2 logit factor), which moves P_ij by a
+factor 2^|dt|.  LSE uses the unrounded p: its bar is the stated 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tiled_attention_03_amd import binding as fa
+from tiled_attention_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dequant(x8, descale):
+    return oracle.e4m3_decode(x8.view(torch.uint8).numpy()) * descale
+
+
+def make_fp8_case(B, H, Sq, Sk, D, layout, mask, seed):
+    shp_q = (B, H, Sq, D) if layout == "BNSD" else (B, Sq, H * D)
+    shp_k = (B, H, Sk, D) if layout == "BNSD" else (B, Sk, H * D)
+    q8, qs = inputs.fp8_quantize(inputs.randn(shp_q, torch.float32, seed))
+    k8, ks = inputs.fp8_quantize(inputs.randn(shp_k, torch.float32, seed + 1))
+    v8, vs = inputs.fp8_quantize(inputs.randn(shp_k, torch.float32, seed + 2))
+    g = torch.Generator().manual_seed(seed)
+    pr = inputs.Problem(f"fp8_{seed}", B, H, Sq, Sk, D, layout, torch.float64, 1.0 / math.sqrt(D),
+                        torch.from_numpy(dequant(q8, qs)), torch.from_numpy(dequant(k8, ks)),
+                        torch.from_numpy(dequant(v8, vs)))
+    if "causal" in mask:
+        pr.causal = True
+    if "explicit" in mask:
+        pr.explicit_mask = torch.rand(B, 1, Sq, Sk, generator=g) < 0.7
+    if "modality" in mask:
+        pr.q_modality = torch.randint(0, 2, (B, Sq), generator=g, dtype=torch.int8)
+        pr.k_modality = torch.randint(0, 2, (B, Sk), generator=g, dtype=torch.int8)
+        pr.modality_allow = torch.tensor([[1, 1], [0, 1]], dtype=torch.bool)
+    if "padding" in mask:
+        lens = torch.randint(1, Sk + 1, (B,), generator=g)
+        pr.key_valid = torch.arange(Sk)[None, :] < lens[:, None]
+    if "alibi" in mask:
+        pr.alibi_slopes = inputs.alibi_slopes(H)
+    if "dense" in mask:
+        pr.pse = torch.randn(1, H, Sq, Sk, generator=g)
+    return pr, (q8, k8, v8), (qs, ks, vs)
+
+
+def run_fp8(pr, t8, scales):
+    q8, k8, v8 = (t.to(DEV) for t in t8)
+    kw = fa.problem_kwargs(pr, DEV)
+    o, lse = fa.fwd_fp8(q8, k8, v8, *scales, heads=pr.heads, layout=pr.layout, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def bnsd(x, pr):
+    x = np.asarray(x, dtype=np.float64)
+    return oracle.bsh_to_bnsd(x, pr.heads) if pr.layout == "BSH" else x
+
+
+def check_fp8(pr, t8, scales, o, lse, heads=None):
+    q, k, v = (bnsd(t.numpy(), pr) for t in (pr.q, pr.k, pr.v))
+    qa = bnsd(np.abs(oracle.e4m3_decode(t8[0].view(torch.uint8).numpy())), pr)
+    ka = bnsd(np.abs(oracle.e4m3_decode(t8[1].view(torch.uint8).numpy())), pr)
+    c = pr.scale * math.log2(math.e) * scales[0] * scales[1]
+    got = bnsd(o.float().cpu().numpy(), pr)
+    lg = lse.cpu().double().numpy()
+    masks = oracle.problem_masks(pr)
+    D = pr.head_dim
+    worst = 0.0
+    for b in range(pr.batch):
+        for h in (range(pr.heads) if heads is None else heads):
+            s = oracle.head_scores(q, k, pr.scale, b, h, oracle._masks(masks))
+            P, L = oracle.softmax_rows(s)
+            O = P @ v[b, h]
+            vis = P > 0
+            av = np.abs(v[b, h])
+            dt = 2 * D * 2.0 ** -24 * (qa[b, h] @ ka[b, h].T) * c
+            bound = (2.0 ** -4 * P) @ av + (2.0 ** -10 * P.max(axis=1, keepdims=True)) * (vis @ av)
+            bound += (P * (np.exp2(dt) - 1.0)) @ av + 2.0 ** -8 * np.abs(O) + 1e-6
+            e = np.abs(got[b, h] - O)
+            worst = max(worst, float((e / bound).max()))
+            assert np.all(e <= bound), (b, h, float(e.max()))
+            dead = np.isneginf(L)
+            assert np.array_equal(np.isneginf(lg[b, h]), dead)
+            if (~dead).any():
+                assert np.abs(lg[b, h][~dead] - L[~dead]).max() <= 1e-3
+            assert np.all(got[b, h][dead] == 0)
+    print(f"  O: worst error / bound {worst:.3f}")
+
+
+CASES = []
+_s = 3000
+for D in (64, 128):
+    for (Sq, Sk) in ((7, 65), (64, 64), (200, 333)):
+        for mask in ("none", "causal", "causal+alibi"):
+            CASES.append((1, 2, Sq, Sk, D, "BNSD", mask, _s))
+            _s += 10
+for mask in ("padding", "explicit", "dense", "modality", "causal+padding+alibi"):
+    CASES.append((2, 3, 97, 150, 128, "BNSD", mask, _s))
+    _s += 10
+CASES.append((2, 2, 160, 96, 128, "BSH", "causal", _s))
+CASES.append((1, 4, 1024, 1024, 128, "BNSD", "causal+alibi", _s + 10))
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,layout,mask,seed", CASES,
+                         ids=[f"D{c[4]}-{c[5]}-{c[2]}x{c[3]}-{c[6]}" for c in CASES])
+def test_fp8_forward(B, H, Sq, Sk, D, layout, mask, seed):
+    pr, t8, sc = make_fp8_case(B, H, Sq, Sk, D, layout, mask, seed)
+    o, lse = run_fp8(pr, t8, sc)
+    assert o.dtype == torch.bfloat16
+    check_fp8(pr, t8, sc, o, lse)
+
+
+def test_fp8_long_sequence_sampled_heads():
+    """The long workload's shape (B=1, H=32, S=8192, D=128, causal + ALiBi) in fp8,
+    checked on two heads the oracle computes whole."""
+    pr, t8, sc = make_fp8_case(1, 32, 8192, 8192, 128, "BNSD", "causal+alibi", 3900)
+    o, lse = run_fp8(pr, t8, sc)
+    check_fp8(pr, t8, sc, o, lse, heads=(0, 31))
+
+
+def test_fp8_no_keys_and_repeatable():
+    pr, t8, sc = make_fp8_case(1, 2, 40, 0, 128, "BNSD", "none", 3950)
+    o, lse = run_fp8(pr, t8, sc)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    pr, t8, sc = make_fp8_case(1, 2, 300, 300, 128, "BNSD", "causal", 3960)
+    o1, l1 = run_fp8(pr, t8, sc)
+    o2, l2 = run_fp8(pr, t8, sc)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

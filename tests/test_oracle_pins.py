@@ -728,3 +728,18 @@ def test_bias_gradient_central_differences(extra):
     np.testing.assert_allclose(dbias.sum(axis=3), 0, atol=1e-12)
     if extra.get("causal"):
         assert np.all(dbias[..., np.triu_indices(Sq, 1, Sk)[0], np.triu_indices(Sq, 1, Sk)[1]] == 0)
+
+
+# ----------------------------------------------------------------------------------
+# fp8 inputs: the e4m3 decoding the fp8 forward's oracle inputs go through
+
+def test_e4m3_decode_all_codes_against_torch():
+    codes = np.arange(256)
+    got = oracle.e4m3_decode(codes)
+    want = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], want[~nan])
+    # a few values written out: 1.0, the largest normal, the smallest subnormal, -2
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+    assert got[0xC0] == -2.0

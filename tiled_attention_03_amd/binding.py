@@ -17,15 +17,17 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
-FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 FA_BNSD, FA_BSH = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_EXPLICIT, FA_MASK_MODALITY, FA_MASK_PADDING = 0, 1, 2, 4, 8
 FA_PSE_NONE, FA_PSE_ALIBI, FA_PSE_DENSE = 0, 1, 2
 
 ENTRY_POINTS = ("fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep", "fa_bwd_main",
-                "fa_bwd_post", "fa_maxsim", "fa_status_str", "fa_abi_version")
+                "fa_bwd_post", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8", "fa_maxsim",
+                "fa_status_str", "fa_abi_version")
 
-_DTYPES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+_DTYPES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
+           torch.float8_e4m3fn: FA_FP8_E4M3}
 _LAYOUTS = {"BNSD": FA_BNSD, "BSH": FA_BSH}
 
 
@@ -102,6 +104,9 @@ def _load():
         "fa_bwd_main": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "fa_bwd_post": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "fa_maxsim": [ctypes.POINTER(FaMaxsimProblem), vp, vp, vp, vp, vp],
+        "fa_fwd_fp8_workspace_size": [P, ctypes.POINTER(sz)],
+        "fa_fwd_fp8": [P, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                       sz, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -285,6 +290,27 @@ def fwd(q, k, v, *, heads: int, layout: str = "BNSD", out=None, lse=None, **kw):
     l = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _stream()),
            "fa_fwd")
+    return o, l
+
+
+def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, *, heads: int,
+            layout: str = "BNSD", workspace=None, **kw):
+    """Forward with float8_e4m3fn inputs (real value = element * descale):
+    returns (O bf16 in q's layout, LSE float32 [B,H,S_q])."""
+    _contig(q, k, v)
+    p, keep = make_problem(q, k, heads=heads, layout=layout, **kw)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
+        raise ValueError("v must match k's shape and q's dtype")
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    l = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check(lib.fa_fwd_fp8_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+               "fa_fwd_fp8_workspace_size")
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.fa_fwd_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), float(q_descale),
+                          float(k_descale), float(v_descale), _ptr(o), _ptr(l), _ptr(workspace),
+                          workspace.numel(), _stream()), "fa_fwd_fp8")
     return o, l
 
 

@@ -30,14 +30,16 @@ fa_status check_problem(const fa_problem *p) {
   if (p->batch < 0 || p->head_num < 0 || p->seq_q < 0 || p->seq_k < 0 || p->head_dim <= 0)
     return FA_ERR_INVALID_ARG;
   if (p->layout != FA_BNSD && p->layout != FA_BSH) return FA_ERR_INVALID_ARG;
-  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16 && p->dtype != FA_FP8_E4M3)
+    return FA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
   if (!(p->keep_prob > 0.f && p->keep_prob <= 1.f)) return FA_ERR_INVALID_ARG;   // NaN too
-  if (p->keep_prob < 1.f && p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (p->keep_prob < 1.f && (p->dtype == FA_F32 || p->dtype == FA_FP8_E4M3))
+    return FA_ERR_UNSUPPORTED;
   if (p->reserved0 != 0) return FA_ERR_INVALID_ARG;
   if (p->dpse) {
     if (p->pse_kind != FA_PSE_DENSE || !aligned16(p->dpse)) return FA_ERR_INVALID_ARG;
-    if (p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (p->dtype == FA_F32 || p->dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
   }
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
   const uint32_t known = FA_MASK_CAUSAL | FA_MASK_EXPLICIT | FA_MASK_MODALITY | FA_MASK_PADDING;
@@ -138,6 +140,7 @@ size_t delta_bytes(const fa_problem *p) {
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 fa_status workspace_ok(const fa_problem *p, const void *ws, size_t bytes) {
+  if (p->dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;   // no fp8 backward
   if (bytes < delta_bytes(p)) return FA_ERR_WORKSPACE;
   if (!tensor_ok(ws)) return FA_ERR_INVALID_ARG;
   return FA_OK;
@@ -165,7 +168,9 @@ const char *fa_status_str(fa_status s) {
 fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *v, void *o,
                  float *lse, hipStream_t stream) {
   fa_status st = check_problem(p);
-  if (st != FA_OK || empty_problem(p)) return st;
+  if (st != FA_OK) return st;
+  if (p->dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;   // fa_fwd_fp8
+  if (empty_problem(p)) return FA_OK;
   if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse)
     return FA_ERR_INVALID_ARG;
   Params r = make_params(p);
@@ -178,6 +183,7 @@ fa_status fa_bwd_workspace_size(const fa_problem *p, size_t *bytes) {
   if (!bytes) return FA_ERR_INVALID_ARG;
   fa_status st = check_problem(p);
   if (st != FA_OK) return st;
+  if (p->dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
   *bytes = empty_problem(p) ? 0 : delta_bytes(p);
   return FA_OK;
 }
@@ -240,6 +246,38 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
   if ((st = fa_bwd_main(p, q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, stream)) != FA_OK)
     return st;
   return fa_bwd_post(p, q, k, v, lse, dout, dq, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_fp8_workspace_size(const fa_problem *p, size_t *bytes) {
+  if (!bytes) return FA_ERR_INVALID_ARG;
+  fa_status st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (p->dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (empty_problem(p)) { *bytes = 0; return FA_OK; }
+  *bytes = round256(fwd_fp8_workspace_bytes(make_params(p)));
+  return FA_OK;
+}
+
+fa_status fa_fwd_fp8(const fa_problem *p, const void *q, const void *k, const void *v,
+                     float q_descale, float k_descale, float v_descale, void *o, float *lse,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (p->dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
+  if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
+    return FA_ERR_INVALID_ARG;
+  if (empty_problem(p)) return FA_OK;
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse)
+    return FA_ERR_INVALID_ARG;
+  Params r = make_params(p);
+  const size_t need = fwd_fp8_workspace_bytes(r);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (need > 0 && !tensor_ok(workspace)) return FA_ERR_INVALID_ARG;
+  r.q = q; r.k = k; r.v = v; r.o = o; r.lse = lse;
+  r.fp8_qk = q_descale * k_descale;
+  r.fp8_v = v_descale;
+  r.vt = workspace;
+  return hip_status(launch_fwd_fp8(r, stream));
 }
 
 fa_status fa_maxsim(const fa_maxsim_problem *p, const void *q, const void *d, float *rowmax,

@@ -63,6 +63,9 @@ struct Params {
   int grad_f32;
   // optional bias gradient, float32 contiguous [B, H, Sq, Sk]
   float *dpse;
+  // fp8 forward: descale products (q * k and v) and the permuted V^T workspace
+  float fp8_qk, fp8_v;
+  void *vt;
 };
 
 // Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random

@@ -11,6 +11,10 @@ namespace fa {
 
 // Forward, bf16/f16 MFMA path (D = 64 or 128).
 hipError_t launch_fwd_mfma(const Params &p, int dtype, hipStream_t s);
+// Forward, fp8 (OCP e4m3) inputs, D = 64 or 128: a pre-pass writes the
+// permuted V^T tiles into p.vt, then the MFMA kernel; O is bf16.
+hipError_t launch_fwd_fp8(const Params &p, hipStream_t s);
+size_t fwd_fp8_workspace_bytes(const Params &p);
 // Forward, fp32 path (D = 32, 64 or 128): fp32 FMA throughout.
 hipError_t launch_fwd_f32(const Params &p, hipStream_t s);
 

@@ -190,3 +190,13 @@ def maxsim_case(B, Lq, Ld, D, dtype, seed, q_mask=None, d_mask=None) -> MaxSimCa
         raise ValueError(kind)
 
     return MaxSimCase(f"maxsim_b{B}lq{Lq}ld{Ld}d{D}", q, d, mask(q_mask, Lq), mask(d_mask, Ld))
+
+
+def fp8_quantize(x: torch.Tensor):
+    """Per-tensor e4m3 quantization of a real tensor: descale = amax / 448 and
+    x8 = round-to-nearest-even(x / descale) as torch.float8_e4m3fn.  The real
+    input the fp8 path stands for is then x8 * descale (not x)."""
+    xf = x.float()
+    amax = float(xf.abs().max()) if xf.numel() else 0.0
+    descale = amax / 448.0 if amax > 0 else 1.0
+    return (xf / descale).to(torch.float8_e4m3fn).contiguous(), descale
