@@ -82,7 +82,9 @@
  * writes nothing.  FA_ERR_INVALID_ARG: null pointer where one is needed,
  * negative sizes, H*D mismatch, M out of range, bad enum,
  * keep_prob outside (0, 1], reserved0 != 0, dpse set without a dense pse or
- * misaligned.  FA_ERR_UNSUPPORTED: keep_prob < 1 with F32, dpse with F32, a
+ * misaligned.  FA_ERR_UNSUPPORTED: scale < 0 (the kernels take a row's
+ * maximum over raw scores before scaling), keep_prob < 1 with F32 or fp8,
+ * dpse with F32 or fp8, a
  * head_dim the kernels do not cover (F16/BF16: 64 or 128; F32: 32, 64 or
  * 128).  FA_ERR_WORKSPACE: workspace
  * too small.  FA_ERR_HIP: a HIP launch reported an error.
@@ -164,7 +166,8 @@ fa_status fa_fwd(const fa_problem *p, const void *q, const void *k, const void *
 /* Forward with fp8 inputs (page 1, tuning section: pure fp8, experimental).
  * p->dtype must be FA_FP8_E4M3: q, k, v hold OCP e4m3 bytes (1 sign, 4
  * exponent bits with bias 7, 3 mantissa bits; no infinities; the value of a
- * byte times its tensor's descale factor is the real input).  O is bf16 in
+ * byte times its tensor's descale factor is the real input; the three
+ * descale factors must be finite and positive).  O is bf16 in
  * Q's layout, LSE float32 [B,H,S_q], both as for fa_fwd, for the real inputs.
  * Masks and bias as for fa_fwd; D = 64 or 128; keep_prob must be 1.
  * The probabilities that multiply V are rounded to e4m3 (p = exp2 of the

@@ -97,6 +97,7 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
     ({"pse_kind": fa.FA_PSE_DENSE}, fa.FA_ERR_INVALID_ARG),
     ({"pse_kind": 5}, fa.FA_ERR_INVALID_ARG),
     ({"scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
+    ({"scale": -0.125}, fa.FA_ERR_UNSUPPORTED),
     ({"reserved0": 1}, fa.FA_ERR_INVALID_ARG),
     ({"dpse": 1 << 20}, fa.FA_ERR_INVALID_ARG),                       # no dense pse
     ({"dpse": (1 << 20) + 4, "pse_kind": fa.FA_PSE_DENSE, "pse": 1 << 20}, fa.FA_ERR_INVALID_ARG),
@@ -202,6 +203,8 @@ def test_fp8_entry_points_validate():
     assert call_fwd_fp8(p8, ws_bytes=n.value - 1) == fa.FA_ERR_WORKSPACE
     assert call_fwd_fp8(p8, ws=None, ws_bytes=n.value) == fa.FA_ERR_INVALID_ARG
     assert call_fwd_fp8(p8, scales=(1.0, float("inf"), 1.0)) == fa.FA_ERR_INVALID_ARG
+    assert call_fwd_fp8(p8, scales=(-1.0, 1.0, 1.0)) == fa.FA_ERR_INVALID_ARG
+    assert call_fwd_fp8(p8, scales=(1.0, 1.0, 0.0)) == fa.FA_ERR_INVALID_ARG
     assert call_fwd_fp8(base_problem(dtype=fa.FA_FP8_E4M3, keep_prob=0.9)) == fa.FA_ERR_UNSUPPORTED
     assert call_fwd_fp8(base_problem(dtype=fa.FA_FP8_E4M3, head_dim=96)) == fa.FA_ERR_UNSUPPORTED
     # empty problems need nothing

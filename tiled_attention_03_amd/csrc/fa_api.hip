@@ -33,6 +33,9 @@ fa_status check_problem(const fa_problem *p) {
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16 && p->dtype != FA_FP8_E4M3)
     return FA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
+  // the kernels take a row's max over raw scores and then scale it, which
+  // needs scale >= 0
+  if (p->scale < 0.f) return FA_ERR_UNSUPPORTED;
   if (!(p->keep_prob > 0.f && p->keep_prob <= 1.f)) return FA_ERR_INVALID_ARG;   // NaN too
   if (p->keep_prob < 1.f && (p->dtype == FA_F32 || p->dtype == FA_FP8_E4M3))
     return FA_ERR_UNSUPPORTED;
@@ -264,7 +267,8 @@ fa_status fa_fwd_fp8(const fa_problem *p, const void *q, const void *k, const vo
   fa_status st = check_problem(p);
   if (st != FA_OK) return st;
   if (p->dtype != FA_FP8_E4M3) return FA_ERR_INVALID_ARG;
-  if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
+  if (!(isfinite(q_descale) && q_descale > 0.f) || !(isfinite(k_descale) && k_descale > 0.f) ||
+      !(isfinite(v_descale) && v_descale > 0.f))
     return FA_ERR_INVALID_ARG;
   if (empty_problem(p)) return FA_OK;
   if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse)

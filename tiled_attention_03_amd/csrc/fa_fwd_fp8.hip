@@ -101,8 +101,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(Params p, int n_qti
   constexpr int KI = kBN * D / 1024 / NW;   // K tile: 1 KB wave loads per wave
   constexpr int VI = D * kBN / 1024 / NW;   // V^T tile: likewise
   static_assert(KI >= 1 && VI >= 1, "tile must split over the waves");
-  __shared__ __attribute__((aligned(16))) uint8_t K0[kBN * D], K1[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint8_t V0[D * kBN], V1[D * kBN];
+  __shared__ __attribute__((aligned(16))) uint8_t K0[kBN * D], K1[kBN * D], K2[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint8_t V0[D * kBN], V1[D * kBN], V2[D * kBN];
   __shared__ int kv_range[2];
 
   const int BH = p.B * p.H;
@@ -299,15 +299,156 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(Params p, int n_qti
     vm_wait_barrier();
   };
 
-  if (kt_begin < kt_end) load_tile(kt_begin, K0, V0);
+  // ---- fast range [kt_begin, f_end): full tiles that need no per-element work
+  // in any wave of the workgroup, with one ALiBi direction (below every row).
+  // Only without mask tensors and dense bias; the other tiles run `step`.
+  int f_end = kt_begin;
+  if (!dense && !f_exp && !f_pad && !f_mod) {
+    f_end = min(kt_end, p.Sk / kBN);                          // full tiles
+    if (causal || alibi) f_end = min(f_end, (q0 + 1) / kBN);   // k0 + 63 <= q0
+    f_end = max(f_end, kt_begin);
+  }
+  f_end = __builtin_amdgcn_readfirstlane(f_end);
+
+  // generic tiles [f_end, kt_end), one per step
+  if (f_end < kt_end) load_tile(f_end, K0, V0);
   vm_wait_barrier();
   {
-    int kt = kt_begin;
+    int kt = f_end;
     for (; kt + 1 < kt_end; kt += 2) {
       step(kt, BufIdx<0>{});
       step(kt + 1, BufIdx<1>{});
     }
     if (kt < kt_end) step(kt, BufIdx<0>{});
+  }
+
+  // ---- pipelined fast phase over [kt_begin, f_end): step n computes the
+  // scores of tile n+1 (MFMA) interleaved with tile n's exponentials (VALU),
+  // then tile n's P V (MFMA) interleaved with tile n+1's logits and row max.
+  // Three buffers: tile n (P V), tile n+1 (scores), tile n+2 (loading).
+  const int n_fast = f_end - kt_begin;
+  // Fast tiles lie below every row (ALiBi direction +1).  Their scores stay in
+  // raw units with the key-dependent part of the bias added, u = s + ar * jr
+  // (jr = 32 kb + 8 (r / 4) + r % 4, a per-register constant; ar = slope / c):
+  // the base-2 logit is c u + lane_base with lane_base = slope (k0 + 4 g - i),
+  // which the max and the exponent's argument take as a per-lane constant.
+  const float ar = alibi ? sl2 / c_log2 : 0.f;
+  float lane_base = 0.f;                // of the tile whose scores sit in the other register set
+  auto fold = [&](f32x16 (&sc)[2], int k0) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float u = fmaf(ar, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), sc[kb][r]);
+        sc[kb][r] = u;
+        mx = fmaxf(mx, u);
+      }
+    lane_base = (alibi ? sl2 : 0.f) * (float)(k0 + 4 * g - my_i);
+    return max_lane_pair(fmaf(mx, c_log2, lane_base));
+  };
+  auto rescale = [&](float mx) __attribute__((always_inline)) {
+    const bool grow = mx > m_run + kTau8;
+    float alpha = 1.f;
+    if (grow) {
+      alpha = exp2_fast(m_run - mx);
+      m_run = mx;
+    }
+    l_run *= alpha;
+    if (__any(grow)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+  };
+  auto kbuf = [&](auto bi) -> uint8_t * {
+    constexpr int B = decltype(bi)::value;
+    return B == 0 ? K0 : (B == 1 ? K1 : K2);
+  };
+  auto vbuf = [&](auto bi) -> uint8_t * {
+    constexpr int B = decltype(bi)::value;
+    return B == 0 ? V0 : (B == 1 ? V1 : V2);
+  };
+  auto fast_step = [&](int n, auto cur, auto nxt, auto ld, f32x16 (&sc)[2], f32x16 (&sn)[2])
+                       __attribute__((always_inline)) {
+    const bool has_next = n + 1 < n_fast;
+    if (n + 2 < n_fast) load_tile(kt_begin + n + 2, kbuf(ld), vbuf(ld));
+    // operands of the next tile's scores, all read up front
+    i32x8 ka[KS][2];
+    if (has_next) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = 32 * kb + lr;
+          ka[t][kb] = read32(kbuf(nxt), row, D, 4 * t + 2 * g, swz_k<D>(row));
+        }
+    }
+    // exponent argument of element u: c u + (lane_base - m_run)
+    const float off = lane_base - (m_run == -INFINITY ? 0.f : m_run);
+    float part = 0.f;
+    i32x8 pk;
+    constexpr int NG = 2 * KS;        // score MFMAs of the next tile
+    constexpr int EPG = 8 / NG;       // packed dwords (4 probabilities each) per group
+    static_assert(NG * EPG == 8, "the 8 packed dwords split over the groups");
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    // the MFMA-dense part at raised issue priority: the other workgroup's wave on
+    // this SIMD fills the gaps with its VALU work
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (has_next) sn[gi & 1] = mac_fp8(ka[gi >> 1][gi & 1], qf[gi >> 1], sn[gi & 1]);
+#pragma unroll
+      for (int e = 0; e < EPG; ++e) {
+        const int dw = gi * EPG + e, kb = dw >> 2, rq = dw & 3;
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          x[t] = exp2_fast(fmaf(sc[kb][4 * rq + t], c_log2, off));
+          part += x[t];
+        }
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+        pk[dw] = wd;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += part;
+    // P V of this tile, then the next tile's logits, max and rescale
+    i32x8 va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 32 * db + lr;
+      va[db] = read32(vbuf(cur), row, kBN, 2 * g, swz_v(row));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = mac_fp8(va[db], pk, acc[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    if (has_next) rescale(fold(sn, (kt_begin + n + 1) * kBN));
+    vm_wait_barrier();
+  };
+  if (n_fast > 0) {
+    load_tile(kt_begin, K0, V0);
+    if (n_fast > 1) load_tile(kt_begin + 1, K1, V1);
+    vm_wait_barrier();
+    f32x16 sA[2] = {f32x16{}, f32x16{}}, sB[2];
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + lr;
+        sA[kb] = mac_fp8(read32(K0, row, D, 4 * t + 2 * g, swz_k<D>(row)), qf[t], sA[kb]);
+      }
+    rescale(fold(sA, kt_begin * kBN));
+    for (int n = 0; n < n_fast; n += 6) {
+      fast_step(n, BufIdx<0>{}, BufIdx<1>{}, BufIdx<2>{}, sA, sB);
+      if (n + 1 < n_fast) fast_step(n + 1, BufIdx<1>{}, BufIdx<2>{}, BufIdx<0>{}, sB, sA);
+      if (n + 2 < n_fast) fast_step(n + 2, BufIdx<2>{}, BufIdx<0>{}, BufIdx<1>{}, sA, sB);
+      if (n + 3 < n_fast) fast_step(n + 3, BufIdx<0>{}, BufIdx<1>{}, BufIdx<2>{}, sB, sA);
+      if (n + 4 < n_fast) fast_step(n + 4, BufIdx<1>{}, BufIdx<2>{}, BufIdx<0>{}, sA, sB);
+      if (n + 5 < n_fast) fast_step(n + 5, BufIdx<2>{}, BufIdx<0>{}, BufIdx<1>{}, sB, sA);
+    }
   }
 
   // ---- O = acc * v_descale / l (bf16) and LSE
