@@ -477,9 +477,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 template <typename T, int D, bool DROP, bool EXTRA>
 __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8;
+  constexpr int QRB = 2;   // k-steps of K / V row operands read ahead of their MFMAs
   constexpr int ES = (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KBQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KBQ * D];
+  // each buffer its own LDS variable, named statically by every access: the
+  // compiler's wait-count pass can then tell a read of the current tile from
+  // the next tile's loads in flight
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KBQ * D], K1[KBQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[KBQ * D], V1[KBQ * D];
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
@@ -544,9 +548,6 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     tile_load<D, KBQ, NWB>(vdst, Vr, voff, base, w);
   };
 
-  if (kt_end > 0) gload(0, Ks[0], Vs[0]);
-  vm_wait_barrier();
-
   // per-lane LDS byte offsets: K/V rows (A operands) and K^T reads
   uint32_t ro[KS], to[2 * DB];
 #pragma unroll
@@ -554,13 +555,14 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
 
-  // One key tile per step.  This kernel keeps a runtime buffer index (a
-  // statically unrolled pair of steps needs more registers than it has
-  // here), so its LDS reads also wait for the next tile's loads.
-  for (int kt = 0, cur = 0; kt < kt_end; ++kt, cur ^= 1) {
-    const uint16_t *ks = Ks[cur];
-    const uint16_t *vs = Vs[cur];
-    if (kt + 1 < kt_end) gload(kt + 1, Ks[cur ^ 1], Vs[cur ^ 1]);
+  // One key tile per step.  GEN: the per-element (general) code is compiled in;
+  // the fast phase's steps carry none of it, which keeps their register
+  // footprint within two waves per SIMD.  The LDS offsets pass through an
+  // empty asm statement each step, so one set of offset registers serves both
+  // buffers.
+  auto body = [&](int kt, const uint16_t *ks, const uint16_t *vs, auto gen_tag)
+                  __attribute__((always_inline)) {
+    constexpr bool GEN = decltype(gen_tag)::value;
     const int k0 = kt * KBQ;
     // fast or general tile; tiles hidden from this wave (at most one per
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
@@ -568,6 +570,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     bool general = f_elem || dense || DROP || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq);
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
+    if (!GEN) general = false;   // the fast phase only visits tiles fast for every wave
     {
       const float off = (alibi ? sl2 * (float)(k0 + 4 * g - my_i) : 0.f) - lse2;
       // one 32-key block at a time (LSE is known: no row max to wait for)
@@ -575,16 +578,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
       for (int jb = 0; jb < 2; ++jb) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int t0 = 0; t0 < KS; t0 += 4) {
-          u32x4 ka[4], va[4];
+        for (int t0 = 0; t0 < KS; t0 += QRB) {
+          u32x4 ka[QRB], va[QRB];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < QRB; ++t) {
             ka[t] = read_row_at<D>(ks, 32 * jb, ro[t0 + t]);
             va[t] = read_row_at<D>(vs, 32 * jb, ro[t0 + t]);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < QRB; ++t) {
             s = Mfma<T>::mac(ka[t], qf[t0 + t], s);
             dp = Mfma<T>::mac(va[t], gf[t0 + t], dp);
           }
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
             const float pr = exp2_fast(fmaf(u, c_log2, off));
             dp[r] = pr * (dp[r] - dlt);
           }
-        } else {
+        } else if constexpr (GEN) {
           // keys 4t .. 4t + 3 of a register group share one Philox call
           uint32_t keep[4] = {0u, 0u, 0u, 0u};
           if (DROP) {
@@ -636,6 +639,43 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
       }
     }
     vm_wait_barrier();
+  };
+
+  // fast range [0, f_end): full tiles every row of the workgroup sees whole
+  // (below the causal diagonal; ALiBi direction +1), without mask tensors,
+  // dense bias or dropout; the rest, [f_end, kt_end), first, one per step
+  int f_end = 0;
+  if (!f_elem && !dense && !DROP && q0 + QBQ <= p.Sq) {
+    f_end = min(kt_end, p.Sk / KBQ);
+    if (causal || alibi) f_end = min(f_end, (q0 + 1) / KBQ);
+  }
+  f_end = __builtin_amdgcn_readfirstlane(f_end);
+  if (f_end < kt_end) gload(f_end, K0, V0);
+  vm_wait_barrier();
+  for (int kt = f_end, cur = 0; kt < kt_end; ++kt, cur ^= 1) {
+    opaque(ro);
+    opaque(to);
+    if (kt + 1 < kt_end) gload(kt + 1, cur ? K0 : K1, cur ? V0 : V1);
+    body(kt, cur ? K1 : K0, cur ? V1 : V0, std::true_type{});
+  }
+  if (f_end > 0) {
+    gload(0, K0, V0);
+    vm_wait_barrier();
+  }
+  auto fstep = [&](int kt, auto buf) __attribute__((always_inline)) {
+    constexpr int B = decltype(buf)::value;
+    opaque(ro);
+    opaque(to);
+    if (kt + 1 < f_end) gload(kt + 1, B ? K0 : K1, B ? V0 : V1);
+    body(kt, B ? K1 : K0, B ? V1 : V0, std::false_type{});
+  };
+  {
+    int kt = 0;
+    for (; kt + 1 < f_end; kt += 2) {
+      fstep(kt, BufIdx<0>{});
+      fstep(kt + 1, BufIdx<1>{});
+    }
+    if (kt < f_end) fstep(kt, BufIdx<0>{});
   }
 
   // dQ = scale * acc; element (db, r): column 32db + 8(r/4) + 4g + r%4
