@@ -577,6 +577,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         f32x16 s = f32x16{}, dp = f32x16{};
+        // fast steps: MFMA runs at raised issue priority, so the other wave on
+        // the SIMD fills their gaps with its VALU work
+        if (!GEN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t0 = 0; t0 < KS; t0 += QRB) {
           u32x4 ka[QRB], va[QRB];
@@ -592,6 +595,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
             dp = Mfma<T>::mac(va[t], gf[t0 + t], dp);
           }
         }
+        if (!GEN) __builtin_amdgcn_s_setprio(0);
         // element r: key k0 + 32jb + 8(r/4) + 4g + r%4, query my_i
         if (!general) {
 #pragma unroll
@@ -626,6 +630,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
           }
         }
         // dQ^T += K^T . dS^T over this block's two 16-key chunks
+        if (!GEN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const u32x4 pd = pack8<T>(dp, 8 * hh);
@@ -636,6 +641,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[db] = Mfma<T>::mac(kop[db], pd, acc[db]);
         }
+        if (!GEN) __builtin_amdgcn_s_setprio(0);
       }
     }
     vm_wait_barrier();
