@@ -397,3 +397,25 @@ def test_bias_gradient(B, H, Sq, Sk, D, dtype, layout, mask, kp, seed):
     g = gpu_bwd(pr, o, lse)
     for a, b in zip((dq, dk, dv), g):
         assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------------
+# the fp32 path against the 16-bit path on the same values
+
+@pytest.mark.parametrize("mask", ["none", "causal+alibi", "padding"])
+def test_fp32_path_agrees_with_bf16_path(mask):
+    """bf16 inputs, and the same values as float32: the two GPU paths (MFMA with
+    16-bit operands, and fp32 FMA throughout) agree within the bf16 bar."""
+    pr16 = make_case(2, 2, 150, 170, 64, torch.bfloat16, "BNSD", mask, 2500)
+    pr32 = make_case(2, 2, 150, 170, 64, torch.bfloat16, "BNSD", mask, 2500)
+    pr32.dtype = torch.float32
+    pr32.q, pr32.k, pr32.v, pr32.do = (t.float() for t in (pr16.q, pr16.k, pr16.v, pr16.do))
+    o16, l16 = gpu_fwd(pr16)
+    o32, l32 = gpu_fwd(pr32)
+    g16 = gpu_bwd(pr16, o16, l16)
+    g32 = gpu_bwd(pr32, o32, l32)
+    assert o32.dtype == torch.float32
+    assert_close("O", o16, o32.double().cpu().numpy(), torch.bfloat16)
+    assert_lse(l16, l32.double().cpu().numpy())
+    for name, a, b in zip(("dQ", "dK", "dV"), g16, g32):
+        assert_close(name, a, b.double().cpu().numpy(), torch.bfloat16)
