@@ -106,7 +106,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   const int it_end = (p.Sq + QB - 1) / QB;
 
   // staging: Q and dO tiles go straight to LDS (rows past S_q read as zeros);
-  // LSE and delta of the block pass through 32 lanes' registers.
+  // LSE and delta of the block pass through 32 lanes' registers.  The loaded
+  // values are first used when they are stored to LDS at the end of the step
+  // (nothing reads them earlier), so the step never waits for the global
+  // loads it has just issued.
   float st_lse = 0.f, st_dlt = 0.f;
   uint32_t voff[TileGeom<D, QB, NWB>::PER_WAVE];
   tile_offsets<D, QB, NWB>(voff, qrow_b, w, l);
@@ -116,15 +119,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     tile_load<D, QB, NWB>(gdst, Gr, voff, base, w);
     if (tid < QB) {
       const int i = it * QB + tid;
-      const float v = i < p.Sq ? p.lse[rbase + i] : -INFINITY;
-      st_lse = (v == -INFINITY) ? INFINITY : v * kLog2e;   // dead rows give P = 0
+      st_lse = i < p.Sq ? p.lse[rbase + i] : -INFINITY;
       st_dlt = i < p.Sq ? p.delta[rbase + i] : 0.f;
     }
   };
   auto sstore = [&](int buf) {
     if (tid < QB) {
-      lse_s[buf][tid] = st_lse;
-      lam_s[buf][tid] = st_lse + sl2 * (float)tid;
+      const float ls = st_lse == -INFINITY ? INFINITY : st_lse * kLog2e;   // dead rows give P = 0
+      lse_s[buf][tid] = ls;
+      lam_s[buf][tid] = ls + sl2 * (float)tid;
       dlt_s[buf][tid] = st_dlt;
     }
   };

@@ -95,6 +95,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   __shared__ uint32_t tsum[kMaxTiles];  // per key tile: bits 0-7 modality set of valid keys,
                                         // bit 8 some key invalid or past S_k
   __shared__ int16_t tlist[kMaxTiles];  // generic tiles, then fast tiles
+  __shared__ uint32_t fpair[kMaxTiles]; // fast tiles n and n+1 in one word (0 past the end)
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
@@ -485,6 +486,13 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // ==== fast phase: software pipeline over list entries n_gen .. n_all-1
   const int n_fast = n_all - n_gen;
   auto ftile = [&](int n) __attribute__((always_inline)) { return tile_at(n_gen + n); };
+  // The fast tiles again, pairs of consecutive entries packed in one word, so a
+  // step learns both tiles it loads from a single LDS read.  Written here and
+  // read only after the barrier that ends the first fast step's set-up.
+  for (int i = tid; i < n_fast; i += C::NT) {
+    const uint32_t nxt = i + 1 < n_fast ? (uint32_t)(uint16_t)tlist[n_gen + i + 1] : 0u;
+    fpair[i] = (uint32_t)(uint16_t)tlist[n_gen + i] | (nxt << 16);
+  }
   // Logit of element r of block (rb, kb) of a fast tile: t = c_log2 * s + lane_off[rb]
   // (base-2 units), with the ALiBi term's per-register part folded into s.  The
   // tile lies wholly below (+1) or above (-1) the diagonal for every row of the
@@ -542,8 +550,9 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     const uint16_t *vs = B ? V1 : V0;   // V of tile n
     opaque(ro);
     opaque(to);
-    const int kt1 = n + 1 < n_fast ? ftile(n + 1) : 0;
-    if (n + 2 < n_fast) load_tile(ftile(n + 2), B ? K1 : K0, Kr);
+    const uint32_t pr = n + 1 < n_fast ? __builtin_amdgcn_readfirstlane(fpair[n + 1]) : 0u;
+    const int kt1 = (int)(pr & 0xffffu);
+    if (n + 2 < n_fast) load_tile((int)(pr >> 16), B ? K1 : K0, Kr);
     if (n + 1 < n_fast) load_tile(kt1, B ? V0 : V1, Vr);
     float alpha[RB], off[RB];
     update_max(mx, alpha);
