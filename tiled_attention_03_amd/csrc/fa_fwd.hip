@@ -207,12 +207,16 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   __syncthreads();
 
   // ---- tile lists.  Workgroup-level class of tile kt: 0 not visited,
-  // 1 generic, 2 fast (no per-element work for any wave of the workgroup).
+  // 1 generic, 2 fast (no per-element work for any wave of the workgroup, or
+  // a causal-band tile whose only per-element work is the causal rule: the
+  // fast phase masks those, and they come first in it).
+  static_assert(C::BM <= 2 * BN, "the fast phase masks at most its first two tiles");
+  const bool band_fast = causal && c_log2 > 0.f && !f_pad && !f_mod;
   auto wg_class = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BN;
     bool fast = !dense && !f_exp && !DROP && k0 + BN <= p.Sk;
-    if (causal && k0 + BN - 1 > q0) fast = false;
-    if (alibi && !(k0 + BN - 1 <= q0 || (!causal && k0 >= q0 + C::BM - 1))) fast = false;
+    if (causal && k0 + BN - 1 > q0) fast = fast && band_fast;
+    else if (alibi && !(k0 + BN - 1 <= q0 || (!causal && k0 >= q0 + C::BM - 1))) fast = false;
     if (f_pad || f_mod) {
       if (!use_summary) return 1;
       const uint32_t ts = tsum[kt], kset = ts & 0xffu;
@@ -496,14 +500,18 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // Logit of element r of block (rb, kb) of a fast tile: t = c_log2 * s + lane_off[rb]
   // (base-2 units), with the ALiBi term's per-register part folded into s.  The
   // tile lies wholly below (+1) or above (-1) the diagonal for every row of the
-  // workgroup.  fold_max folds the tile starting at key k0 into s (coefficient 0
-  // without ALiBi: no branch, the scores stay in place) and leaves lane_off and
-  // the row max (combined over the lane pair) in mx; `part` selects a quarter of
-  // the elements (0..3) or all of them (-1), so the work can be spread over MFMA
-  // sections.
+  // workgroup, or (causal rule) straddles it, where every visible key is at or
+  // below the row, so the +1 form holds for them.  fold_max folds the tile
+  // starting at key k0 into s (coefficient 0 without ALiBi: no branch, the
+  // scores stay in place) and leaves lane_off and the row max (combined over
+  // the lane pair) in mx; `part` selects a quarter of the elements (0..3) or
+  // all of them (-1), so the work can be spread over MFMA sections.  MASK
+  // applies the causal rule per element (raw score -inf where key > row, which
+  // needs c_log2 > 0); on a tile wholly below the diagonal it changes nothing.
   auto fold_max = [&](f32x16 (&sc)[RB][KBN], int k0, int part, float (&lane_off)[RB],
-                      float (&mx)[RB]) __attribute__((always_inline)) {
-    const int adir = k0 + BN - 1 <= q0 ? 1 : -1;
+                      float (&mx)[RB], auto mask) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask)::value;
+    const int adir = (causal || k0 + BN - 1 <= q0) ? 1 : -1;
     const float a = alibi ? adir * sl2c : 0.f;
     constexpr int NE = 16 * KBN;
     const int e0 = part < 0 ? 0 : part * NE / 4, e1 = part < 0 ? NE : (part + 1) * NE / 4;
@@ -513,11 +521,15 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         lane_off[rb] = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i[rb]) : 0.f;
         mx[rb] = -INFINITY;
       }
+      // element (kb, r) holds key k0 + 4g + c with c = 32kb + 8(r/4) + r%4
+      const int lim = causal ? my_i[rb] - k0 - 4 * g : 0x7fffffff;
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
         if (e < e0 || e >= e1) continue;
         const int kb = e / 16, r = e % 16;
-        sc[rb][kb][r] = fmaf(a, (float)(32 * kb + 8 * (r >> 2) + (r & 3)), sc[rb][kb][r]);
+        const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+        const float v = fmaf(a, (float)c, sc[rb][kb][r]);
+        sc[rb][kb][r] = (MASK && c > lim) ? -INFINITY : v;
         mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
       }
       if (part < 0 || part == 3) mx[rb] = max_lane_pair(fmaf(mx[rb], c_log2, lane_off[rb]));
@@ -535,7 +547,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   vm_wait_barrier();
   if (n_fast > 0) {
     scores(K0, sA);
-    fold_max(sA, ftile(0) * BN, -1, loA, mxA);
+    fold_max(sA, ftile(0) * BN, -1, loA, mxA, std::bool_constant<true>{});
   }
   lds_barrier();   // every wave is done with K0 before the first step refills it
 
@@ -543,7 +555,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // tile n+1 (into sn) with their fold and max (into lon, mxn), O += P V of
   // tile n.  Buffer parity B: K_{n+1} in K[1-B], V_n in V[B].
   auto fast_step = [&](int n, auto buf, f32x16 (&s)[RB][KBN], float (&lo)[RB], float (&mx)[RB],
-                       f32x16 (&sn)[RB][KBN], float (&lon)[RB], float (&mxn)[RB])
+                       f32x16 (&sn)[RB][KBN], float (&lon)[RB], float (&mxn)[RB], auto mask)
                        __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
     const uint16_t *kn = B ? K0 : K1;   // K of tile n+1
@@ -629,19 +641,22 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb][db] = Mfma<T>::mac(va[c][db], pk[rb][c], acc[rb][db]);
-      fold_max(sn, kt1 * BN, c * 4 / NC, lon, mxn);
+      fold_max(sn, kt1 * BN, c * 4 / NC, lon, mxn, mask);
       __builtin_amdgcn_sched_barrier(0x0004);
     }
     __builtin_amdgcn_s_setprio(0);
     vm_wait_barrier();
   };
-  {
-    int n = 0;
+  if (n_fast > 0) {
+    // causal-band tiles lead the list: tile 0 was folded with the mask above,
+    // step 0 folds tile 1 with it, and the steps after it need none
+    fast_step(0, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, std::bool_constant<true>{});
+    int n = 1;
     for (; n + 1 < n_fast; n += 2) {
-      fast_step(n, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB);
-      fast_step(n + 1, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA);
+      fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, std::bool_constant<false>{});
+      fast_step(n + 1, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, std::bool_constant<false>{});
     }
-    if (n < n_fast) fast_step(n, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB);
+    if (n < n_fast) fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, std::bool_constant<false>{});
   }
 
   // ---- epilogue: O = acc / l, LSE
