@@ -138,6 +138,15 @@ def test_fp8_long_sequence_sampled_heads():
     check_fp8(pr, t8, sc, o, lse, heads=(0, 31))
 
 
+def test_fp8_scale_zero_with_alibi():
+    """scale = 0 leaves the ALiBi bias as the only logit; the fast form, which
+    divides the slope by the scale, stands aside."""
+    pr, t8, sc = make_fp8_case(1, 2, 300, 300, 128, "BNSD", "causal+alibi", 3970)
+    pr.scale = 0.0
+    o, lse = run_fp8(pr, t8, sc)
+    check_fp8(pr, t8, sc, o, lse)
+
+
 def test_fp8_no_keys_and_repeatable():
     pr, t8, sc = make_fp8_case(1, 2, 40, 0, 128, "BNSD", "none", 3950)
     o, lse = run_fp8(pr, t8, sc)

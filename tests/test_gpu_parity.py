@@ -162,6 +162,28 @@ def test_zero_inputs():
     check_bwd(pr, o, lse)
 
 
+@pytest.mark.parametrize("D,dtype,mask", [(128, torch.bfloat16, "causal+alibi"),
+                                          (64, torch.float16, "causal"),
+                                          (128, torch.float16, "causal"),
+                                          (64, torch.bfloat16, "causal+alibi")])
+def test_causal_band_several_workgroups(D, dtype, mask):
+    """Causal problems whose diagonal band tiles and blocks take the pipelined
+    paths with a per-element mask: several 128-row and 128-key workgroups."""
+    pr = make_case(1, 2, 512, 512, D, dtype, "BNSD", mask, 960 + D)
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
+@pytest.mark.parametrize("mask", ["alibi", "causal+alibi", "causal"])
+def test_scale_zero(mask):
+    """scale = 0: the logits are the bias alone (uniform rows without ALiBi);
+    the fast ALiBi forms divide the slope by the scale, so they stand aside."""
+    pr = make_case(1, 2, 300, 300, 128, torch.bfloat16, "BNSD", mask, 970)
+    pr.scale = 0.0
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_large_scores_exercise_running_max(D):
     pr = make_case(1, 2, 300, 300, D, torch.bfloat16, "BNSD", "causal", 904 + D)

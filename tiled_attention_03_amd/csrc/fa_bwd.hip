@@ -32,6 +32,7 @@
 // while step n is multiplied, with one barrier per step; blocks the mask hides
 // entirely are skipped.
 #include <algorithm>
+#include <climits>
 
 #include "fa_launch.h"
 #include "fa_tile.h"
@@ -134,14 +135,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 
   // Query blocks come in two groups.  Fast blocks need no per-element work
   // for any key of the workgroup (full blocks, no mask tensors or dense bias,
-  // and under the causal rule or ALiBi every row at or below every key); they
-  // form the range [f0, f1) and run software-pipelined.  The other blocks
-  // (the causal diagonal band, the S_q tail, masked problems) run one block
-  // per step with per-wave classification.  The sums over blocks do not
-  // depend on the order.
+  // and under ALiBi every row at or below every key), or, under the causal
+  // rule, only the causal rule itself: the band of blocks on the diagonal,
+  // which lead the range and whose steps mask per element.  They form the
+  // range [f0, f1) and run software-pipelined.  The other blocks (the S_q
+  // tail, masked problems, ALiBi without the causal rule near the diagonal)
+  // run one block per step with per-wave classification.  The sums over
+  // blocks do not depend on the order.
+  static_assert(KB / QB == 4, "the masked steps cover a band of four blocks");
   int f0 = it_end, f1 = it_end;
   if (!f_elem && !dense && !DROP && j0 + KB <= p.Sk) {
-    const int first = (causal || alibi) ? max(it_begin, (j0 + KB - 1 + QB - 1) / QB) : it_begin;
+    const int first = (alibi && !causal) ? max(it_begin, (j0 + KB - 1 + QB - 1) / QB) : it_begin;
     const int last = p.Sq / QB;   // full blocks only
     if (first < last) { f0 = first; f1 = last; }
   }
@@ -340,9 +344,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
   }
   if (n_fast > 0) scores(Q0, G0, sA, dpA);
 
+  // MASK: the causal rule per element (P = 0 for a key past its query);
+  // on a block wholly below the diagonal it changes nothing.
   auto fast_step = [&](int n, auto buf, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn,
-                       f32x4 (&lam)[4], f32x4 (&dl)[4], f32x4 (&lamn)[4], f32x4 (&dln)[4])
-                       __attribute__((always_inline)) {
+                       f32x4 (&lam)[4], f32x4 (&dl)[4], f32x4 (&lamn)[4], f32x4 (&dln)[4],
+                       auto mask) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask)::value;
     constexpr int B = decltype(buf)::value, N1 = (B + 1) % 3, N2 = (B + 2) % 3;
     const uint16_t *qs = B == 0 ? Q0 : B == 1 ? Q1 : Q2;      // block n
     const uint16_t *gs = B == 0 ? G0 : B == 1 ? G1 : G2;
@@ -354,6 +361,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     opaque(to);
     const int i0 = (f0 + n) * QB;
     const float L = sl2 * (float)(my_j - i0);
+    // element r holds query i0 + 4g + c, c = 8(r/4) + r%4: masked when c < lim
+    const int lim = causal ? my_j - i0 - 4 * g : INT_MIN;
     // Order fixed by scheduling fences (only scalar work may cross them): the
     // first half of the next block's operand reads up front, the rest one
     // k-step before they are needed; per k-step its two score products, then
@@ -408,7 +417,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
       }
 #pragma unroll
       for (int r = t * EPS; r < (t + 1) * EPS; ++r) {
-        const float pr = exp2_fast(fmaf(s[r], c_log2, L - lam[r >> 2][r & 3]));
+        float pr = exp2_fast(fmaf(s[r], c_log2, L - lam[r >> 2][r & 3]));
+        if (MASK) pr = 8 * (r >> 2) + (r & 3) < lim ? 0.f : pr;
         s[r] = pr;
         dp[r] = pr * (dp[r] - dl[r >> 2][r & 3]);
       }
@@ -433,14 +443,21 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     if (has_next2) sstore(N2);
     vm_wait_barrier();
   };
-  // six steps per trip: three buffers times two register sets
-  for (int n = 0; n < n_fast; n += 6) {
-    fast_step(n, BufIdx<0>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
-    if (n + 1 < n_fast) fast_step(n + 1, BufIdx<1>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
-    if (n + 2 < n_fast) fast_step(n + 2, BufIdx<2>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
-    if (n + 3 < n_fast) fast_step(n + 3, BufIdx<0>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
-    if (n + 4 < n_fast) fast_step(n + 4, BufIdx<1>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB);
-    if (n + 5 < n_fast) fast_step(n + 5, BufIdx<2>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA);
+  // the first four steps (the causal band, when the range starts there) mask
+  // per element; then six steps per trip: three buffers times two register sets
+  const std::bool_constant<true> masked;
+  const std::bool_constant<false> plain;
+  if (n_fast > 0) fast_step(0, BufIdx<0>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB, masked);
+  if (n_fast > 1) fast_step(1, BufIdx<1>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA, masked);
+  if (n_fast > 2) fast_step(2, BufIdx<2>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB, masked);
+  if (n_fast > 3) fast_step(3, BufIdx<0>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA, masked);
+  for (int n = 4; n < n_fast; n += 6) {
+    fast_step(n, BufIdx<1>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB, plain);
+    if (n + 1 < n_fast) fast_step(n + 1, BufIdx<2>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA, plain);
+    if (n + 2 < n_fast) fast_step(n + 2, BufIdx<0>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB, plain);
+    if (n + 3 < n_fast) fast_step(n + 3, BufIdx<1>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA, plain);
+    if (n + 4 < n_fast) fast_step(n + 4, BufIdx<2>{}, sA, dpA, sB, dpB, lmA, dlA, lmB, dlB, plain);
+    if (n + 5 < n_fast) fast_step(n + 5, BufIdx<0>{}, sB, dpB, sA, dpA, lmB, dlB, lmA, dlA, plain);
   }
 
   // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
@@ -558,19 +575,24 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
 
-  // One key tile per step.  GEN: the per-element (general) code is compiled in;
-  // the fast phase's steps carry none of it, which keeps their register
-  // footprint within two waves per SIMD.  The LDS offsets pass through an
-  // empty asm statement each step, so one set of offset registers serves both
-  // buffers.
-  auto body = [&](int kt, const uint16_t *ks, const uint16_t *vs, auto gen_tag)
+  // One key tile per step.  Mode 2 (GEN): the per-element (general) code is
+  // compiled in; the fast modes carry none of it, which keeps their register
+  // footprint within two waves per SIMD.  Mode 1 (BAND): a fast tile on the
+  // causal diagonal, where the causal rule zeroes P for keys above each row
+  // (every visible key is at or below the row, so the fast ALiBi form holds).
+  // The LDS offsets pass through an empty asm statement each step, so one set
+  // of offset registers serves both buffers.
+  auto body = [&](int kt, const uint16_t *ks, const uint16_t *vs, auto mode)
                   __attribute__((always_inline)) {
-    constexpr bool GEN = decltype(gen_tag)::value;
+    constexpr bool GEN = decltype(mode)::value == 2;
+    constexpr bool BAND = decltype(mode)::value == 1;
     const int k0 = kt * KBQ;
     // fast or general tile; tiles hidden from this wave (at most one per
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
     // accumulation stays unconditional
-    bool general = f_elem || dense || DROP || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq);
+    // (the fast ALiBi form folds slope / c_log2 into raw scores: c_log2 > 0)
+    bool general = f_elem || dense || DROP || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
+                   (alibi && !(c_log2 > 0.f));
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
     if (!GEN) general = false;   // the fast phase only visits tiles fast for every wave
@@ -601,11 +623,14 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
         if (!GEN) __builtin_amdgcn_s_setprio(0);
         // element r: key k0 + 32jb + 8(r/4) + 4g + r%4, query my_i
         if (!general) {
+          const int lim = my_i - k0 - 4 * g;   // BAND: keys past the row have c > lim
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
+            const int c = 32 * jb + 8 * (r >> 2) + (r & 3);
             float u = s[r];
-            if (alibi) u = fmaf(sl2c, (float)(32 * jb + 8 * (r >> 2) + (r & 3)), u);
-            const float pr = exp2_fast(fmaf(u, c_log2, off));
+            if (alibi) u = fmaf(sl2c, (float)c, u);
+            float pr = exp2_fast(fmaf(u, c_log2, off));
+            if (BAND) pr = c > lim ? 0.f : pr;
             dp[r] = pr * (dp[r] - dlt);
           }
         } else if constexpr (GEN) {
@@ -652,20 +677,33 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
 
   // fast range [0, f_end): full tiles every row of the workgroup sees whole
   // (below the causal diagonal; ALiBi direction +1), without mask tensors,
-  // dense bias or dropout; the rest, [f_end, kt_end), first, one per step
-  int f_end = 0;
-  if (!f_elem && !dense && !DROP && q0 + QBQ <= p.Sq) {
+  // dense bias or dropout.  Under the causal rule alone the full tiles on the
+  // diagonal, [f_end, b_end), run the fast code with the causal mask (it needs
+  // c_log2 > 0); the rest, [b_end, kt_end), take the general code.  Those two
+  // groups go first, one per step.
+  int f_end = 0, b_end = 0;
+  if (!f_elem && !dense && !DROP && q0 + QBQ <= p.Sq && (!alibi || c_log2 > 0.f)) {
     f_end = min(kt_end, p.Sk / KBQ);
+    b_end = f_end;
     if (causal || alibi) f_end = min(f_end, (q0 + 1) / KBQ);
+    if (!causal || !(c_log2 > 0.f)) b_end = f_end;
   }
   f_end = __builtin_amdgcn_readfirstlane(f_end);
+  b_end = __builtin_amdgcn_readfirstlane(b_end);
   if (f_end < kt_end) gload(f_end, K0, V0);
   vm_wait_barrier();
-  for (int kt = f_end, cur = 0; kt < kt_end; ++kt, cur ^= 1) {
+  int cur = 0;
+  for (int kt = f_end; kt < b_end; ++kt, cur ^= 1) {
     opaque(ro);
     opaque(to);
     if (kt + 1 < kt_end) gload(kt + 1, cur ? K0 : K1, cur ? V0 : V1);
-    body(kt, cur ? K1 : K0, cur ? V1 : V0, std::true_type{});
+    body(kt, cur ? K1 : K0, cur ? V1 : V0, std::integral_constant<int, 1>{});
+  }
+  for (int kt = b_end; kt < kt_end; ++kt, cur ^= 1) {
+    opaque(ro);
+    opaque(to);
+    if (kt + 1 < kt_end) gload(kt + 1, cur ? K0 : K1, cur ? V0 : V1);
+    body(kt, cur ? K1 : K0, cur ? V1 : V0, std::integral_constant<int, 2>{});
   }
   if (f_end > 0) {
     gload(0, K0, V0);
@@ -676,7 +714,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     opaque(ro);
     opaque(to);
     if (kt + 1 < f_end) gload(kt + 1, B ? K0 : K1, B ? V0 : V1);
-    body(kt, B ? K1 : K0, B ? V1 : V0, std::false_type{});
+    body(kt, B ? K1 : K0, B ? V1 : V0, std::integral_constant<int, 0>{});
   };
   {
     int kt = 0;

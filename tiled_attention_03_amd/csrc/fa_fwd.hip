@@ -159,6 +159,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   const float c_log2 = p.scale_log2;
   const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;   // slope in log2 units
   const float sl2c = alibi ? sl2 / c_log2 : 0.f;                 // slope in raw-score units
+  const bool raw_ok = !alibi || c_log2 > 0.f;   // the fast forms fold sl2c into raw scores
   const bool f_pad = flags & FA_MASK_PADDING, f_mod = flags & FA_MASK_MODALITY;
   const bool f_exp = flags & FA_MASK_EXPLICIT;
 
@@ -214,7 +215,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   const bool band_fast = causal && c_log2 > 0.f && !f_pad && !f_mod;
   auto wg_class = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BN;
-    bool fast = !dense && !f_exp && !DROP && k0 + BN <= p.Sk;
+    bool fast = raw_ok && !dense && !f_exp && !DROP && k0 + BN <= p.Sk;
     if (causal && k0 + BN - 1 > q0) fast = fast && band_fast;
     else if (alibi && !(k0 + BN - 1 <= q0 || (!causal && k0 >= q0 + C::BM - 1))) fast = false;
     if (f_pad || f_mod) {
@@ -354,7 +355,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     const int k0 = kt * BN;
 
     int cls = qw < p.Sq ? kFast : kDead;
-    if (dense || f_exp || k0 + BN > p.Sk) cls = max(cls, (int)kGeneral);
+    if (dense || f_exp || k0 + BN > p.Sk || !raw_ok) cls = max(cls, (int)kGeneral);
     if (causal) {
       if (k0 > qw + WR - 1) cls = kDead;
       else if (k0 + BN - 1 > qw) cls = max(cls, (int)kGeneral);
