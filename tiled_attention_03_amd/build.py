@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_f32.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_maxsim.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.hip", "fa_f32.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_split.hip", "fa_maxsim.hip",
+           "fa_fwd_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -809,6 +809,7 @@ hipError_t launch_q(const Params &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s) {
+  if (bwd_kv_split_eligible(p)) return launch_bwd_kv_split(p, dtype, s);
   if (dtype == FA_BF16) {
     if (p.D == 64) return launch_kv<__bf16, 64>(p, s);
     if (p.D == 128) return launch_kv<__bf16, 128>(p, s);

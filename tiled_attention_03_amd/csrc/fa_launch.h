@@ -20,8 +20,13 @@ hipError_t launch_fwd_f32(const Params &p, hipStream_t s);
 
 // Backward step 1 (any dtype): delta_i = sum_d dO_id O_id.
 hipError_t launch_bwd_prep(const Params &p, int dtype, hipStream_t s);
-// Backward step 2: dK, dV (key-tile pass).
+// Backward step 2: dK, dV (key-tile pass).  The producer/consumer form
+// serves the problems bwd_kv_split_eligible accepts (causal rule with or
+// without ALiBi, or no mask or bias; no dropout or bias gradient);
+// launch_bwd_kv_mfma picks it for them and the one-role pass otherwise.
 hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s);
+bool bwd_kv_split_eligible(const Params &p);
+hipError_t launch_bwd_kv_split(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_bwd_kv_f32(const Params &p, hipStream_t s);
 // Backward step 3: dQ (query-tile pass), written in dtype/layout.
 hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s);
