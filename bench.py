@@ -28,7 +28,7 @@ METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 _CSRC = "tiled_attention_03_amd/csrc/"
 KERNEL_SOURCES = {   # files whose text decides each timed kernel's code
     "fwd": [_CSRC + f for f in ("fa_fwd.hip", "fa_tile.h", "fa_common.h")],
-    "bwd_main": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
+    "bwd_main": [_CSRC + f for f in ("fa_bwd.hip", "fa_bwd_split.hip", "fa_tile.h", "fa_common.h")],
     "bwd_post": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
     "maxsim": [_CSRC + f for f in ("fa_maxsim.hip", "fa_tile.h", "fa_common.h")],
 }
