@@ -174,6 +174,22 @@ def test_causal_band_several_workgroups(D, dtype, mask):
     check_bwd(pr, o, lse)
 
 
+SPLIT = [(2, 3, 300, 300, 128, torch.bfloat16, "BSH", "causal+alibi", 980),
+         (2, 3, 257, 250, 64, torch.float16, "BSH", "causal", 981),
+         (2, 3, 100, 260, 128, torch.bfloat16, "BSH", "none", 982),
+         (1, 3, 260, 140, 64, torch.bfloat16, "BNSD", "causal+alibi", 983)]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,seed", SPLIT,
+                         ids=[f"{c[6]}-D{c[4]}-{c[2]}x{c[3]}-{c[7]}" for c in SPLIT])
+def test_producer_consumer_key_pass(B, H, Sq, Sk, D, dtype, layout, mask, seed):
+    """Problems the producer/consumer key pass serves (causal rule with or without
+    ALiBi, or no mask): several heads and batches, both layouts, ragged S_q and S_k."""
+    pr = make_case(B, H, Sq, Sk, D, dtype, layout, mask, seed)
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
 @pytest.mark.parametrize("mask", ["alibi", "causal+alibi", "causal"])
 def test_scale_zero(mask):
     """scale = 0: the logits are the bias alone (uniform rows without ALiBi);
