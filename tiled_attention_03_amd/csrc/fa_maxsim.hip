@@ -24,26 +24,43 @@
 //     least one valid token: padding is never read.  Meanwhile the query
 //     block is copied to LDS by direct-to-LDS loads (swizzled rows; rows past
 //     L_q are zeros).
-//  2. A tile is consumed in blocks of 64 dimensions (4 MFMA k-steps, one
-//     16-byte load per lane per k-step); RING blocks are in flight ahead of
-//     the one being multiplied, across the wave's tiles.  The MFMA computes
-//     S^T = D_tile Q^T, so lane l holds query column l % 32 and 16 document
-//     rows, and a tile's masked max is a per-lane max over registers.
+//  2. A tile is consumed in blocks of 64 dimensions; RING blocks are in
+//     flight ahead of the one being multiplied, across the wave's tiles.  The
+//     products are 16x16x32 MFMAs, S^T = D Q^T per 16 documents and 16
+//     queries: their A operand takes 16 document rows (lane l: row l % 16,
+//     8 dimensions at 8 (l / 16)), so one 16-byte load per lane reads 16 rows
+//     x 64 contiguous bytes.  Loads that each touch 32 rows (the 32x32x16
+//     operand) streamed at about 30 GB/s per workgroup, half the rate of
+//     loads of the same bytes over fewer rows.  Lane l holds query column
+//     l % 16 and 4 document rows of each product, so a tile's masked max is
+//     a per-lane max over registers, then over the 4 lanes of a column.
 //  3. The two lanes of a query column and the NW waves are merged; rowmax is
 //     written, and with a single query block the score as well (fixed-order
 //     sum; the result is bitwise repeatable).  With several query blocks a
 //     second small kernel forms the scores from rowmax.
 //
-// The dot product's dimension order is permuted the same way on both
-// operands: within a 64-dimension block, k-step t of lane half h covers
-// dimensions 32h + 8t .. 32h + 8t + 7, so that each lane reads 64
-// contiguous bytes of its document row per block and a lane pair covers the
-// row's 128 bytes.
+// Within a 64-dimension block, k-step t covers dimensions 32t .. 32t + 31:
+// lane quarter k = l / 16 holds dimensions 32t + 8k .. 32t + 8k + 7 of its
+// row, on both operands.
 #include "fa_launch.h"
 #include "fa_tile.h"
 
 namespace fa {
 namespace {
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<__bf16> {
+  static __device__ __forceinline__ f32x4 mac(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<_Float16> {
+  static __device__ __forceinline__ f32x4 mac(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
 
 constexpr int kMsNW = 16;          // waves per workgroup
 constexpr int kMsRing = 4;         // 64-dimension blocks in flight per wave
@@ -126,10 +143,9 @@ __global__ __launch_bounds__(NW * 64) void maxsim_kernel(MaxSimParams p, int n_q
   const int total = my_tiles * nblk;
   const __amdgpu_buffer_rsrc_t rd =
       make_rsrc((const T *)p.d + (int64_t)b * p.Ld * D, (uint32_t)p.Ld * rowb);
-  const int hf = lane >> 5, r32 = lane & 31;
-  const uint32_t lane_off = (uint32_t)r32 * rowb + (uint32_t)hf * 64u;
-  const uint32_t q_row = (uint32_t)r32 * rowb;
-  const int q_swz = swz<128>(r32);
+  const int quad = lane >> 4, r16 = lane & 15;
+  // document operand: row r16 of a 16-document group, 16 bytes at 16 quad
+  const uint32_t lane_off = (uint32_t)r16 * rowb + (uint32_t)quad * 16u;
 
   // byte offset of the first row of the wave's ordinal-th listed tile (or past the end)
   auto tile_base = [&](int ordinal) -> uint32_t {
@@ -138,13 +154,17 @@ __global__ __launch_bounds__(NW * 64) void maxsim_kernel(MaxSimParams p, int n_q
     return (uint32_t)t * 32u * rowb;
   };
 
+  // ring slot: operand (dg, t) at [2 dg + t] for document group dg, k-step t
   u32x4 ring[RING][4];
   int is_ord = 0, is_kb = 0;                 // issue side: tile ordinal, block
   uint32_t is_base = tile_base(0);
   auto issue = [&](u32x4 (&dst)[4]) __attribute__((always_inline)) {
     const uint32_t off = is_base + lane_off + (uint32_t)is_kb * 128u;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dst[t] = buf_load16(rd, off + 16u * t);
+    for (int dg = 0; dg < 2; ++dg)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        dst[2 * dg + t] = buf_load16(rd, off + (uint32_t)dg * 16u * rowb + 64u * t);
     if (++is_kb == nblk) {
       is_kb = 0;
       is_base = tile_base(++is_ord);
@@ -155,10 +175,21 @@ __global__ __launch_bounds__(NW * 64) void maxsim_kernel(MaxSimParams p, int n_q
   for (int s = 0; s < RING - 1; ++s) issue(ring[s]);
   vm_wait_barrier();                         // the query block is in LDS
 
-  f32x16 acc;
+  // accumulators (dg, qg): lane l holds query 16 qg + l % 16 and documents
+  // 16 dg + 4 quad + i, i = 0..3
+  f32x4 acc[2][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  float m = -INFINITY;
+  for (int dg = 0; dg < 2; ++dg)
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) acc[dg][qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};      // per query group
+  uint32_t q_row[2];
+  int q_swz[2];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    q_row[qg] = (uint32_t)(16 * qg + r16) * rowb;
+    q_swz[qg] = swz<128>(16 * qg + r16);
+  }
   int c_ord = 0, c_kb = 0;                   // compute side
 
   for (int n0 = 0; n0 < total; n0 += RING) {
@@ -167,20 +198,30 @@ __global__ __launch_bounds__(NW * 64) void maxsim_kernel(MaxSimParams p, int n_q
       issue(ring[(r + RING - 1) % RING]);
       if (n0 + r < total) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int c = c_kb * 8 + hf * 4 + t;
-          const u32x4 bq = *(const u32x4 *)((const char *)Qs + q_row + ((c ^ q_swz) << 4));
-          acc = Mfma<T>::mac(ring[r][t], bq, acc);
+        for (int t = 0; t < 2; ++t) {
+          const int c = c_kb * 8 + t * 4 + quad;
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg) {
+            const u32x4 bq =
+                *(const u32x4 *)((const char *)Qs + q_row[qg] + ((c ^ q_swz[qg]) << 4));
+#pragma unroll
+            for (int dg = 0; dg < 2; ++dg)
+              acc[dg][qg] = Mfma16<T>::mac(ring[r][2 * dg + t], bq, acc[dg][qg]);
+          }
         }
         if (++c_kb == nblk) {
           // tile done: masked max over its 32 documents, then start afresh
           const uint32_t vm = __builtin_amdgcn_readfirstlane(tmask[w][c_ord]);
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int jj = 8 * (q >> 2) + 4 * hf + (q & 3);
-            if ((vm >> jj) & 1u) m = fmaxf(m, acc[q]);
-            acc[q] = 0.f;
-          }
+          for (int dg = 0; dg < 2; ++dg)
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int jj = 16 * dg + 4 * quad + i;
+                if ((vm >> jj) & 1u) m[qg] = fmaxf(m[qg], acc[dg][qg][i]);
+                acc[dg][qg][i] = 0.f;
+              }
           c_kb = 0;
           ++c_ord;
         }
@@ -188,9 +229,14 @@ __global__ __launch_bounds__(NW * 64) void maxsim_kernel(MaxSimParams p, int n_q
     }
   }
 
-  // 3. merge the lane pair of each query column, then the waves
-  m = max_lane_pair(m);
-  if (lane < 32) part[w][lane] = m;
+  // 3. merge the four lanes of each query column, then the waves: lane q < 32
+  //    ends up with query q's max
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    m[qg] = fmaxf(m[qg], __shfl_xor(m[qg], 16, 64));
+    m[qg] = fmaxf(m[qg], __shfl_xor(m[qg], 32, 64));
+  }
+  if (lane < 32) part[w][lane] = lane < 16 ? m[0] : m[1];
   __syncthreads();
   if (w == 0 && lane < 32) {
     float rm = part[0][lane];
