@@ -88,8 +88,10 @@
  * head_dim the kernels do not cover (F16/BF16: 64 or 128; F32: 32, 64 or
  * 128).  FA_ERR_WORKSPACE: workspace
  * too small.  FA_ERR_HIP: a HIP launch reported an error.
- * Sizes of zero are allowed: B, H or S_q == 0 is a no-op; S_k == 0 makes every
- * row masked (O = 0, LSE = -inf, dQ = 0).
+ * Sizes of zero are allowed: B or H == 0 is a no-op; S_q == 0 makes the
+ * forward and the steps other than fa_bwd_main a no-op, while fa_bwd and
+ * fa_bwd_main write dK = dV = 0 (no query sees a key; only dk and dv are
+ * read then); S_k == 0 makes every row masked (O = 0, LSE = -inf, dQ = 0).
  *
  * Synchronisation: calls enqueue work on `stream` and return without waiting.
  * Outputs are valid once the stream reaches that point.  The library keeps

@@ -142,6 +142,31 @@ def test_no_keys_gives_zero_output_and_minus_inf_lse():
     assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
 
 
+@pytest.mark.parametrize("dtype,mask,gf32", [(torch.bfloat16, "causal", False),
+                                             (torch.bfloat16, "none", False),
+                                             (torch.float16, "padding", False),
+                                             (torch.bfloat16, "causal+alibi", True),
+                                             (torch.float32, "none", False)])
+def test_no_queries_gives_zero_key_gradients(dtype, mask, gf32):
+    """S_q = 0 with keys: no query sees a key, so dK = dV = 0 (written, not left as they were)."""
+    pr = make_case(2, 2, 0, 70, 64, dtype, "BNSD", mask, 909)
+    pr.grad_f32 = gf32
+    o, lse = gpu_fwd(pr)
+    assert o.numel() == 0 and lse.numel() == 0
+    q, k, v, do = (t.to(DEV) for t in (pr.q, pr.k, pr.v, pr.do))
+    gdt = torch.float32 if gf32 else dtype
+    dk = torch.full(k.shape, 7.0, dtype=gdt, device=DEV)
+    dv = torch.full(v.shape, 7.0, dtype=gdt, device=DEV)
+    plan = fa.Plan(q, k, heads=pr.heads, layout=pr.layout, **fa.problem_kwargs(pr, DEV))
+    plan.bwd_main(q, k, v, lse, do, dk, dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    dq, dk2, dv2 = gpu_bwd(pr, o, lse)
+    assert dq.numel() == 0 and torch.all(dk2 == 0) and torch.all(dv2 == 0)
+    rq, rk, rv = oracle.problem_bwd(pr)
+    assert np.all(np.asarray(rk) == 0) and np.all(np.asarray(rv) == 0)
+
+
 def test_fully_masked_rows():
     pr = make_case(1, 2, 50, 70, 128, torch.bfloat16, "BNSD", "explicit", 902)
     pr.explicit_mask[:, :, 5] = False

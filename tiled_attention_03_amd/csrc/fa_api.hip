@@ -203,11 +203,27 @@ fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout, void
   return hip_status(launch_bwd_prep(r, p->dtype, stream));
 }
 
+// S_q == 0 with keys: no query attends to any key, so dK = dV = 0.
+bool keys_without_queries(const fa_problem *p) {
+  return p->batch > 0 && p->head_num > 0 && p->seq_q == 0 && p->seq_k > 0;
+}
+
+fa_status zero_kv_grads(const fa_problem *p, void *dk, void *dv, hipStream_t stream) {
+  if (!ktensor_ok(p, dk) || !ktensor_ok(p, dv)) return FA_ERR_INVALID_ARG;
+  const int64_t esize = (p->dtype == FA_F32 || p->grad_f32) ? 4 : 2;
+  const int64_t words = (int64_t)p->batch * p->head_num * p->seq_k * p->head_dim * esize / 4;
+  hipError_t e = launch_zero_words(dk, words, stream);
+  if (e == hipSuccess) e = launch_zero_words(dv, words, stream);
+  return hip_status(e);
+}
+
 fa_status fa_bwd_main(const fa_problem *p, const void *q, const void *k, const void *v,
                       const float *lse, const void *dout, void *dk, void *dv,
                       const void *workspace, size_t workspace_bytes, hipStream_t stream) {
   fa_status st = check_problem(p);
-  if (st != FA_OK || empty_problem(p)) return st;
+  if (st != FA_OK) return st;
+  if (keys_without_queries(p)) return zero_kv_grads(p, dk, dv, stream);
+  if (empty_problem(p)) return FA_OK;
   if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !lse || !tensor_ok(dout) ||
       !ktensor_ok(p, dk) || !ktensor_ok(p, dv))
     return FA_ERR_INVALID_ARG;
@@ -239,7 +255,9 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
   fa_status st = check_problem(p);
-  if (st != FA_OK || empty_problem(p)) return st;
+  if (st != FA_OK) return st;
+  if (keys_without_queries(p)) return zero_kv_grads(p, dk, dv, stream);
+  if (empty_problem(p)) return FA_OK;
   // validate every pointer before the first launch
   if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse ||
       !tensor_ok(dout) || !tensor_ok(dq) || !ktensor_ok(p, dk) || !ktensor_ok(p, dv))

@@ -808,6 +808,13 @@ hipError_t launch_q(const Params &p, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_zero_words(void *dst, int64_t n_words, hipStream_t s) {
+  if (n_words <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((n_words / 4 + 255) / 256 + 1, 4096);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, (float *)dst, n_words);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s) {
   if (bwd_kv_split_eligible(p)) return launch_bwd_kv_split(p, dtype, s);
   if (dtype == FA_BF16) {

@@ -30,6 +30,9 @@ hipError_t launch_bwd_kv_split(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_bwd_kv_f32(const Params &p, hipStream_t s);
 // Backward step 3: dQ (query-tile pass), written in dtype/layout.
 hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s);
+// Zeroes n_words 32-bit words at dst (16-byte aligned): a fill kernel, not a
+// memset node, so that it behaves inside captured graphs.
+hipError_t launch_zero_words(void *dst, int64_t n_words, hipStream_t s);
 hipError_t launch_bwd_q_f32(const Params &p, hipStream_t s);
 
 // MaxSim late-interaction scores (see fa_maxsim in include/fa.h).
