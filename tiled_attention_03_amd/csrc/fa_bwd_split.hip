@@ -56,14 +56,16 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
   constexpr int ES = (int)sizeof(T);
   using G = TileGeom<D, SQB, NPW>;
   constexpr int LPW = 2 * G::PER_WAVE + 1;   // global loads per producer wave per block
-  // Ring of four block slots (blocks n .. n+3), each one variable holding the
-  // Q tile, the dO tile, then LSE and delta of the block's rows; and the
-  // P^T / dS^T exchange (ring of two).  Every access names its buffer
-  // statically, and the four slots are few enough for the compiler's
+  // Ring of six block slots (block b in slot b % 6), each one variable
+  // holding the Q tile, the dO tile, then LSE and delta of the block's rows;
+  // and the P^T / dS^T exchange (ring of two).  Every access names its
+  // buffer statically, and the slots are few enough for the compiler's
   // wait-count pass to track the direct-to-LDS loads into each of them apart,
   // so a read of one slot does not wait for loads into another.
+  constexpr int NSL = 6;
   constexpr int SLOT = 2 * SQB * D + 4 * SQB;   // 16-bit units
-  __shared__ __attribute__((aligned(16))) uint16_t T0[SLOT], T1[SLOT], T2[SLOT], T3[SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t T0[SLOT], T1[SLOT], T2[SLOT], T3[SLOT],
+      T4[SLOT], T5[SLOT];
   __shared__ __attribute__((aligned(16))) u32x4 X0[NPW * 64 * 4], X1[NPW * 64 * 4];
 
   const int BH = p.B * p.H;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
 
   auto slot = [&](auto bi) -> uint16_t * {
     constexpr int B = decltype(bi)::value;
-    return B == 0 ? T0 : B == 1 ? T1 : B == 2 ? T2 : T3;
+    return B == 0 ? T0 : B == 1 ? T1 : B == 2 ? T2 : B == 3 ? T3 : B == 4 ? T4 : T5;
   };
   auto qbuf = [&](auto bi) { return slot(bi); };
   auto gbuf = [&](auto bi) { return slot(bi) + SQB * D; };
@@ -141,15 +143,11 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     for (int t = 0; t < KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
     const float c_log2 = p.scale_log2;
     const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
-    const bool k_tail = j0 + SKB > p.Sk;
-    const bool k_ok = my_j < p.Sk;
 
-    auto produce = [&](int n, auto bi) __attribute__((always_inline)) {
+    // S and dP of the block in slot bi, not interleaved (the first block)
+    auto scores = [&](auto bi, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
       const uint16_t *qs = qbuf(bi), *gs = gbuf(bi);
-      const float *ls = lbuf(bi), *ds = ebuf(bi);
-      const int i0 = (it_begin + n) * SQB;
-      f32x16 s = f32x16{}, dp = f32x16{};
-      f32x4 lv[4], dl[4];
+      s = dp = f32x16{};
 #pragma unroll
       for (int t0 = 0; t0 < KS; t0 += 4) {
         u32x4 qa[4], ga[4];
@@ -158,15 +156,6 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
           qa[t] = read_row_at<D>(qs, 0, ro[t0 + t]);
           ga[t] = read_row_at<D>(gs, 0, ro[t0 + t]);
         }
-        if (t0 + 4 == KS) {
-          // the block's row statistics, behind the last operand reads: they
-          // arrive while the last products run
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            lv[rr] = *(const f32x4 *)&ls[8 * rr + 4 * g];
-            dl[rr] = *(const f32x4 *)&ds[8 * rr + 4 * g];
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -174,40 +163,10 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
           dp = Mfma<T>::mac(ga[t], vf[t0 + t], dp);
         }
       }
-      // element r: query i0 + 4g + c, c = 8(r/4) + r%4; key my_j.  Base-2 logit
-      // t = c_log2 s + slope (my_j - i) - LSE log2e (the ALiBi form holds for
-      // every visible key, which is at or below its row).  Blocks on the
-      // causal diagonal or past S_q or S_k zero the hidden elements; the test
-      // is made once per block, so the other blocks carry no per-element mask.
-      const float L = sl2 * (float)(my_j - i0 - 4 * g);
-      auto elems = [&](auto mask) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask)::value;
-        const int lim = !k_ok ? INT_MAX : causal ? my_j - i0 - 4 * g : INT_MIN;  // c < lim hidden
-        const int qlim = p.Sq - i0 - 4 * g;                                     // c >= qlim hidden
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * rr + q, c = 8 * rr + q;
-            const float off = fmaf(lv[rr][q], -kLog2e, fmaf(-sl2, (float)c, L));
-            float pr = exp2_fast(fmaf(s[r], c_log2, off));
-            if (MASK) pr = (c < lim || c >= qlim) ? 0.f : pr;
-            s[r] = pr;
-            dp[r] = pr * (dp[r] - dl[rr][q]);
-          }
-        }
-      };
-      if ((causal && i0 < j0 + SKB) || k_tail || i0 + SQB > p.Sq) elems(std::true_type{});
-      else elems(std::false_type{});
-      u32x4 *x = xbuf(bi) + l;
-      x[0] = pack8<T>(s, 0);
-      x[64] = pack8<T>(s, 8);
-      x[128] = pack8<T>(dp, 0);
-      x[192] = pack8<T>(dp, 8);
     };
 
-    // end of a step: this wave's loads of the next block have landed (those
-    // of the block after it may still be in flight), its LDS writes are
+    // end of a step: this wave's loads of the block after next have landed
+    // (those issued in this step may still be in flight), its LDS writes are
     // done; then the workgroup barrier
     auto finish = [&](bool more) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
@@ -216,27 +175,96 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    // step n: produce block n from slot n%4 into exchange slot n%2, then load
-    // block n+2 into slot (n+2)%4 (last read by the consumer in step n-1).
-    // The loads go out after this step's LDS reads, so that no read waits for
-    // them.
-    auto pstep = [&](int n, auto bi) __attribute__((always_inline)) {
+
+    // Step n (block n in slot n % 6, its S and dP in s / dp from the step
+    // before): S and dP of block n+1 into sn / dpn, interleaved k-step by
+    // k-step with block n's P and dS (which do not depend on them), in an
+    // order fixed by scheduling fences; block n's P^T / dS^T go to exchange
+    // slot n % 2; then block n+3 is loaded into slot (n+3) % 6, which held
+    // block n-3 (last read in step n-2).  On the last step the scores come
+    // from a stale slot and are unused.
+    //   element r: query i0 + 4g + c, c = 8(r/4) + r%4; key my_j.  Base-2
+    //   logit t = c_log2 s + slope (my_j - i) - LSE log2e (the ALiBi form
+    //   holds for every visible key, which is at or below its row).  MASK
+    //   (the four blocks of the causal band, which lead the range) zeroes
+    //   keys past their query.  Rows past S_q have zero Q and dO rows, so
+    //   their P cannot reach dV or dK; keys past S_k are never stored; and
+    //   outside the band every key is at or below every row, so P stays
+    //   finite there without a mask.
+    constexpr int KPF = 2;                 // operand reads run this many k-steps ahead
+    constexpr int EPS = 16 / KS;           // elements of P / dS per k-step
+    auto pstep = [&](int n, auto bi, auto mask, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn)
+                     __attribute__((always_inline)) {
       constexpr int B = decltype(bi)::value;
+      constexpr bool MASK = decltype(mask)::value;
       opaque(ro);
-      const bool more = n + 2 < nb;
-      if (n < nb) produce(n, bi);
+      const uint16_t *qn = qbuf(BufIdx<(B + 1) % NSL>{}), *gn = gbuf(BufIdx<(B + 1) % NSL>{});
+      const float *ls = lbuf(bi), *ds = ebuf(bi);
+      const int i0 = (it_begin + n) * SQB;
+      const float L = sl2 * (float)(my_j - i0 - 4 * g);
+      const int lim = causal ? my_j - i0 - 4 * g : INT_MIN;   // c < lim is hidden
+      f32x4 lv[4], dl[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        lv[rr] = *(const f32x4 *)&ls[8 * rr + 4 * g];
+        dl[rr] = *(const f32x4 *)&ds[8 * rr + 4 * g];
+      }
+      u32x4 qa[KS], ga[KS];
+#pragma unroll
+      for (int t = 0; t < KPF; ++t) {
+        qa[t] = read_row_at<D>(qn, 0, ro[t]);
+        ga[t] = read_row_at<D>(gn, 0, ro[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0x0004);
+      sn = dpn = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        if (t + KPF < KS) {
+          qa[t + KPF] = read_row_at<D>(qn, 0, ro[t + KPF]);
+          ga[t + KPF] = read_row_at<D>(gn, 0, ro[t + KPF]);
+        }
+        sn = Mfma<T>::mac(qa[t], kf[t], sn);
+        dpn = Mfma<T>::mac(ga[t], vf[t], dpn);
+#pragma unroll
+        for (int r = t * EPS; r < (t + 1) * EPS; ++r) {
+          const int rr = r >> 2, q = r & 3, c = 8 * rr + q;
+          const float off = fmaf(lv[rr][q], -kLog2e, fmaf(-sl2, (float)c, L));
+          float pr = exp2_fast(fmaf(s[r], c_log2, off));
+          if (MASK) pr = c < lim ? 0.f : pr;
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - dl[rr][q]);
+        }
+        __builtin_amdgcn_sched_barrier(0x0004);
+      }
+      u32x4 *x = xbuf(bi) + l;
+      x[0] = pack8<T>(s, 0);
+      x[64] = pack8<T>(s, 8);
+      x[128] = pack8<T>(dp, 0);
+      x[192] = pack8<T>(dp, 8);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) load_block(n + 2, BufIdx<(B + 2) % 4>{});
+      const bool more = n + 3 < nb;
+      if (more) load_block(n + 3, BufIdx<(B + 3) % NSL>{});
       finish(more);
     };
     if (nb > 0) load_block(0, BufIdx<0>{});
     if (nb > 1) load_block(1, BufIdx<1>{});
-    finish(nb > 1);
-    for (int n = 0; n <= nb; n += 4) {
-      pstep(n, BufIdx<0>{});
-      if (n + 1 <= nb) pstep(n + 1, BufIdx<1>{});
-      if (n + 2 <= nb) pstep(n + 2, BufIdx<2>{});
-      if (n + 3 <= nb) pstep(n + 3, BufIdx<3>{});
+    if (nb > 2) load_block(2, BufIdx<2>{});
+    finish(nb > 2);   // blocks 0 and 1 have landed
+    f32x16 sA, dpA, sB, dpB;
+    scores(BufIdx<0>{}, sA, dpA);   // stale when nb == 0, and unused
+    const std::true_type band;
+    const std::false_type plain;
+    if (0 <= nb) pstep(0, BufIdx<0>{}, band, sA, dpA, sB, dpB);
+    if (1 <= nb) pstep(1, BufIdx<1>{}, band, sB, dpB, sA, dpA);
+    if (2 <= nb) pstep(2, BufIdx<2>{}, band, sA, dpA, sB, dpB);
+    if (3 <= nb) pstep(3, BufIdx<3>{}, band, sB, dpB, sA, dpA);
+    for (int n = 4; n <= nb; n += 6) {
+      pstep(n, BufIdx<4>{}, plain, sA, dpA, sB, dpB);
+      if (n + 1 <= nb) pstep(n + 1, BufIdx<5>{}, plain, sB, dpB, sA, dpA);
+      if (n + 2 <= nb) pstep(n + 2, BufIdx<0>{}, plain, sA, dpA, sB, dpB);
+      if (n + 3 <= nb) pstep(n + 3, BufIdx<1>{}, plain, sB, dpB, sA, dpA);
+      if (n + 4 <= nb) pstep(n + 4, BufIdx<2>{}, plain, sA, dpA, sB, dpB);
+      if (n + 5 <= nb) pstep(n + 5, BufIdx<3>{}, plain, sB, dpB, sA, dpA);
     }
   } else {
     // ======================= consumer =======================
@@ -248,7 +276,7 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     for (int db = 0; db < DB; ++db) tr_off<D>(&to[2 * db], 32 * db, l);
 
     // The transposed dO / Q operands of a block are read one step ahead:
-    // block n's tiles have been in LDS since the barrier that ended step n-1,
+    // block n's tiles have been in LDS since the barrier that ended step n-2,
     // so step n reads them after issuing its products, and step n+1 only
     // waits for the exchange reads before its first product.
     u32x4 gt[2][DB], qt[2][DB];
@@ -281,21 +309,23 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       __builtin_amdgcn_sched_barrier(0);
     };
     // step n: consume block n-1 (exchange slot (n-1)%2, operands already in
-    // registers), then read block n's operands from ring slot n%4
+    // registers), then read block n's operands from ring slot n % 6
     auto cstep = [&](int n, auto bi) __attribute__((always_inline)) {
       constexpr int B = decltype(bi)::value;
       opaque(to);
-      if (n >= 1 && n - 1 < nb) consume(BufIdx<(B + 3) % 4>{});
+      if (n >= 1 && n - 1 < nb) consume(BufIdx<(B + NSL - 1) % NSL>{});
       __builtin_amdgcn_sched_barrier(0);
       if (n < nb) prefetch(bi);
       finish();
     };
     finish();   // the producers' set-up barrier
-    for (int n = 0; n <= nb; n += 4) {
+    for (int n = 0; n <= nb; n += NSL) {
       cstep(n, BufIdx<0>{});
       if (n + 1 <= nb) cstep(n + 1, BufIdx<1>{});
       if (n + 2 <= nb) cstep(n + 2, BufIdx<2>{});
       if (n + 3 <= nb) cstep(n + 3, BufIdx<3>{});
+      if (n + 4 <= nb) cstep(n + 4, BufIdx<4>{});
+      if (n + 5 <= nb) cstep(n + 5, BufIdx<5>{});
     }
 
     // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
