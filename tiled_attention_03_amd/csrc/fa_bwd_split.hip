@@ -26,8 +26,9 @@
 // producer; the exchange ring has two.
 //
 // Handles the causal rule with or without ALiBi, and plain (maskless)
-// problems, without dropout or the bias gradient (float32 gradient outputs
-// included); the launcher sends everything else to the one-role key pass.  Under the causal rule every row
+// problems, with or without dropout, without the bias gradient (float32
+// gradient outputs included); the launcher sends everything else to the
+// one-role key pass.  Under the causal rule every row
 // sees key 0, so no row has an empty softmax here and the LSE is finite.
 #include <climits>
 
@@ -50,7 +51,9 @@ __device__ __forceinline__ void stats_load(float *dst, __amdgpu_buffer_rsrc_t rs
                                            voff, (int)soff, 0, 0);
 }
 
-template <typename T, int D>
+// DROP: dropout compiled in (keep_prob < 1); the producer regenerates the
+// Philox keep mask of its elements, as the one-role pass does.
+template <typename T, int D, bool DROP>
 __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p, int n_ktiles) {
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int ES = (int)sizeof(T);
@@ -203,6 +206,24 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       const int i0 = (it_begin + n) * SQB;
       const float L = sl2 * (float)(my_j - i0 - 4 * g);
       const int lim = causal ? my_j - i0 - 4 * g : INT_MIN;   // c < lim is hidden
+      // dropout: the four lanes of a quad hold four consecutive keys and the
+      // same 16 queries, so lane q of the quad draws the Philox words of the
+      // queries with r % 4 == q (one call covers the quad's four keys), packs
+      // the keep bits, and the quad exchanges them; bit 4 rr of kq[q] is then
+      // the keep bit of element 4 rr + q for this lane's key
+      uint32_t kq[4] = {0u, 0u, 0u, 0u};
+      if (DROP) {
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          mine |= dropout_keep4(p, b, h, i0 + 8 * rr + 4 * g + (l & 3), my_j) << (4 * rr);
+        kq[0] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+        kq[1] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+        kq[2] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+        kq[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kq[q] >>= (l & 3);
+      }
       f32x4 lv[4], dl[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -231,8 +252,15 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
           const float off = fmaf(lv[rr][q], -kLog2e, fmaf(-sl2, (float)c, L));
           float pr = exp2_fast(fmaf(s[r], c_log2, off));
           if (MASK) pr = c < lim ? 0.f : pr;
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - dl[rr][q]);
+          if (DROP) {
+            // P o M / keep_prob feeds dV, and dP is masked the same way
+            const float m = dropout_scale(p, (kq[q] >> (4 * rr)) & 1u);
+            s[r] = pr * m;
+            dp[r] = pr * (dp[r] * m - dl[rr][q]);
+          } else {
+            s[r] = pr;
+            dp[r] = pr * (dp[r] - dl[rr][q]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0x0004);
       }
@@ -366,8 +394,12 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
   const int n_ktiles = (p.Sk + SKB - 1) / SKB;
   const int64_t blocks = (int64_t)n_ktiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_kv_split_kernel<T, D>), dim3((unsigned)blocks), dim3(2 * NPW * 64), 0, s,
-                     p, n_ktiles);
+  if (p.dropout)
+    hipLaunchKernelGGL((bwd_kv_split_kernel<T, D, true>), dim3((unsigned)blocks),
+                       dim3(2 * NPW * 64), 0, s, p, n_ktiles);
+  else
+    hipLaunchKernelGGL((bwd_kv_split_kernel<T, D, false>), dim3((unsigned)blocks),
+                       dim3(2 * NPW * 64), 0, s, p, n_ktiles);
   return hipGetLastError();
 }
 
@@ -378,7 +410,7 @@ bool bwd_kv_split_eligible(const Params &p) {
   if (p.mask_flags & other) return false;
   if (p.pse_kind == FA_PSE_DENSE) return false;
   if (p.pse_kind == FA_PSE_ALIBI && !(p.mask_flags & FA_MASK_CAUSAL)) return false;
-  if (p.dropout || p.dpse) return false;
+  if (p.dpse) return false;
   return p.D == 64 || p.D == 128;
 }
 

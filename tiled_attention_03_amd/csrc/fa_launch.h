@@ -22,7 +22,7 @@ hipError_t launch_fwd_f32(const Params &p, hipStream_t s);
 hipError_t launch_bwd_prep(const Params &p, int dtype, hipStream_t s);
 // Backward step 2: dK, dV (key-tile pass).  The producer/consumer form
 // serves the problems bwd_kv_split_eligible accepts (causal rule with or
-// without ALiBi, or no mask or bias; no dropout or bias gradient);
+// without ALiBi, or no mask or bias; dropout allowed, no bias gradient);
 // launch_bwd_kv_mfma picks it for them and the one-role pass otherwise.
 hipError_t launch_bwd_kv_mfma(const Params &p, int dtype, hipStream_t s);
 bool bwd_kv_split_eligible(const Params &p);
