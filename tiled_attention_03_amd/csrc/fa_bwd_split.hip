@@ -22,7 +22,7 @@
 // dK / dV accumulators), so each fits half a SIMD's register file, and the
 // matrix core takes products from whichever wave is ready.  One barrier per
 // step.  Q / dO tiles and the row statistics of a block go straight from
-// global memory into a ring of four LDS buffers, two blocks ahead of the
+// global memory into a ring of six LDS buffers, three blocks ahead of the
 // producer; the exchange ring has two.
 //
 // Handles the causal rule with or without ALiBi, and plain (maskless)
@@ -128,6 +128,12 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
         kf[t] = buf_load16(Kr, off + (16 * t + 8 * g) * ES);
         vf[t] = buf_load16(Vr, off + (16 * t + 8 * g) * ES);
       }
+      // without dropout the dP accumulator starts at the row's delta and V
+      // enters negated, so it ends at delta - dP = -(dP - delta)
+      if constexpr (!DROP) {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) vf[t] ^= 0x80008000u;
+      }
     }
     uint32_t voff[G::PER_WAVE];
     tile_offsets<D, SQB, NPW>(voff, qrow_b, w, l);
@@ -146,11 +152,43 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     for (int t = 0; t < KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
     const float c_log2 = p.scale_log2;
     const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
+    // The S accumulator of element r (query i = i0 + 4g + c, c = 8(r/4) + r%4)
+    // starts at u = -(LSE_i log2e + slope log2e c) / c_log2, so that
+    // c_log2 (S + u) + slope log2e (my_j - i0 - 4g) is the base-2 logit
+    // c_log2 S + slope log2e (my_j - i) - LSE_i log2e with one fma per
+    // element; the per-element constants live in scalar registers.
+    const float inv_c = 1.f / c_log2;
+    const float kA = -kLog2e * inv_c;
+    float cu[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      cu[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                            int, -sl2 * inv_c * (float)(8 * (r >> 2) + (r & 3)))));
+    // start values of block bi's S and dP accumulators
+    auto init_acc = [&](auto bi, f32x16 &s0, f32x16 &dp0) __attribute__((always_inline)) {
+      const float *ls = lbuf(bi), *ds = ebuf(bi);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 lv = *(const f32x4 *)&ls[8 * rr + 4 * g];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s0[4 * rr + q] = fmaf(lv[q], kA, cu[4 * rr + q]);
+      }
+      if constexpr (DROP) {
+        dp0 = f32x16{};
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 dv = *(const f32x4 *)&ds[8 * rr + 4 * g];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dp0[4 * rr + q] = dv[q];
+        }
+      }
+    };
 
     // S and dP of the block in slot bi, not interleaved (the first block)
     auto scores = [&](auto bi, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
       const uint16_t *qs = qbuf(bi), *gs = gbuf(bi);
-      s = dp = f32x16{};
+      init_acc(bi, s, dp);
 #pragma unroll
       for (int t0 = 0; t0 < KS; t0 += 4) {
         u32x4 qa[4], ga[4];
@@ -195,17 +233,50 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     //   outside the band every key is at or below every row, so P stays
     //   finite there without a mask.
     constexpr int KPF = 2;                 // operand reads run this many k-steps ahead
-    constexpr int EPS = 16 / KS;           // elements of P / dS per k-step
+    constexpr int PRE = 4;                 // elements of P / dS before the first product
     auto pstep = [&](int n, auto bi, auto mask, f32x16 &s, f32x16 &dp, f32x16 &sn, f32x16 &dpn)
                      __attribute__((always_inline)) {
       constexpr int B = decltype(bi)::value;
       constexpr bool MASK = decltype(mask)::value;
       opaque(ro);
       const uint16_t *qn = qbuf(BufIdx<(B + 1) % NSL>{}), *gn = gbuf(BufIdx<(B + 1) % NSL>{});
-      const float *ls = lbuf(bi), *ds = ebuf(bi);
+      const float *ds = ebuf(bi);
       const int i0 = (it_begin + n) * SQB;
       const float L = sl2 * (float)(my_j - i0 - 4 * g);
       const int lim = causal ? my_j - i0 - 4 * g : INT_MIN;   // c < lim is hidden
+      // dropout: the four lanes of a quad hold four consecutive keys and the
+      // same 16 queries, so lane q of the quad draws the Philox words of the
+      // queries with r % 4 == q (one call covers the quad's four keys), packs
+      // the keep bits, and the quad exchanges them; bit 4 rr of kq[q] is then
+      // the keep bit of element 4 rr + q for this lane's key
+      // LDS reads first, all in flight together: block n+1's LSE (for the S
+      // start values) and delta (the dP start values), its first KPF operand
+      // k-steps, and under dropout block n's delta
+      f32x4 lvr[4], dl[4];
+      {
+        const float *ln = lbuf(BufIdx<(B + 1) % NSL>{}), *dn = ebuf(BufIdx<(B + 1) % NSL>{});
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) lvr[rr] = *(const f32x4 *)&ln[8 * rr + 4 * g];
+        if constexpr (DROP) {
+          dpn = f32x16{};
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) dl[rr] = *(const f32x4 *)&ds[8 * rr + 4 * g];
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 dv = *(const f32x4 *)&dn[8 * rr + 4 * g];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dpn[4 * rr + q] = dv[q];
+          }
+        }
+      }
+      u32x4 qa[KS], ga[KS];
+#pragma unroll
+      for (int t = 0; t < KPF; ++t) {
+        qa[t] = read_row_at<D>(qn, 0, ro[t]);
+        ga[t] = read_row_at<D>(gn, 0, ro[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0x0004);
       // dropout: the four lanes of a quad hold four consecutive keys and the
       // same 16 queries, so lane q of the quad draws the Philox words of the
       // queries with r % 4 == q (one call covers the quad's four keys), packs
@@ -224,20 +295,30 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
 #pragma unroll
         for (int q = 0; q < 4; ++q) kq[q] >>= (l & 3);
       }
-      f32x4 lv[4], dl[4];
+      // element r of block n: P, then dS (negated without dropout)
+      auto elem = [&](int r) __attribute__((always_inline)) {
+        const int rr = r >> 2, q = r & 3, c = 8 * rr + q;
+        float pr = exp2_fast(fmaf(s[r], c_log2, L));
+        if (MASK) pr = c < lim ? 0.f : pr;
+        if constexpr (DROP) {
+          // P o M / keep_prob feeds dV, and dP is masked the same way
+          const float m = dropout_scale(p, (kq[q] >> (4 * rr)) & 1u);
+          s[r] = pr * m;
+          dp[r] = pr * (dp[r] * m - dl[rr][q]);
+        } else {
+          s[r] = pr;
+          dp[r] = pr * dp[r];   // -dS: the accumulator holds delta - dP
+        }
+      };
+      // the first PRE elements (registers only) cover the reads' latency
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        lv[rr] = *(const f32x4 *)&ls[8 * rr + 4 * g];
-        dl[rr] = *(const f32x4 *)&ds[8 * rr + 4 * g];
-      }
-      u32x4 qa[KS], ga[KS];
-#pragma unroll
-      for (int t = 0; t < KPF; ++t) {
-        qa[t] = read_row_at<D>(qn, 0, ro[t]);
-        ga[t] = read_row_at<D>(gn, 0, ro[t]);
-      }
+      for (int r = 0; r < PRE; ++r) elem(r);
       __builtin_amdgcn_sched_barrier(0x0004);
-      sn = dpn = f32x16{};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sn[4 * rr + q] = fmaf(lvr[rr][q], kA, cu[4 * rr + q]);
+      __builtin_amdgcn_sched_barrier(0x0004);
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         if (t + KPF < KS) {
@@ -247,21 +328,7 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
         sn = Mfma<T>::mac(qa[t], kf[t], sn);
         dpn = Mfma<T>::mac(ga[t], vf[t], dpn);
 #pragma unroll
-        for (int r = t * EPS; r < (t + 1) * EPS; ++r) {
-          const int rr = r >> 2, q = r & 3, c = 8 * rr + q;
-          const float off = fmaf(lv[rr][q], -kLog2e, fmaf(-sl2, (float)c, L));
-          float pr = exp2_fast(fmaf(s[r], c_log2, off));
-          if (MASK) pr = c < lim ? 0.f : pr;
-          if (DROP) {
-            // P o M / keep_prob feeds dV, and dP is masked the same way
-            const float m = dropout_scale(p, (kq[q] >> (4 * rr)) & 1u);
-            s[r] = pr * m;
-            dp[r] = pr * (dp[r] * m - dl[rr][q]);
-          } else {
-            s[r] = pr;
-            dp[r] = pr * (dp[r] - dl[rr][q]);
-          }
-        }
+        for (int r = PRE + t * (16 - PRE) / KS; r < PRE + (t + 1) * (16 - PRE) / KS; ++r) elem(r);
         __builtin_amdgcn_sched_barrier(0x0004);
       }
       u32x4 *x = xbuf(bi) + l;
@@ -356,7 +423,9 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       if (n + 5 <= nb) cstep(n + 5, BufIdx<5>{});
     }
 
-    // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr
+    // dK (scaled) and dV; element r: key jw + 8(r/4) + 4g + r%4, column 32db + lr.
+    // Without dropout the exchanged dS is negated, and so is the scale.
+    const float dks = DROP ? p.scale : -p.scale;
     if (p.grad_f32) {
       float *DKf = (float *)p.dk + koff;
       float *DVf = (float *)p.dv + koff;
@@ -366,7 +435,7 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
         for (int r = 0; r < 16; ++r) {
           const int j = jw + 8 * (r >> 2) + 4 * g + (r & 3);
           if (j < p.Sk) {
-            DKf[(int64_t)j * p.k_ss + 32 * db + lr] = dk[db][r] * p.scale;
+            DKf[(int64_t)j * p.k_ss + 32 * db + lr] = dk[db][r] * dks;
             DVf[(int64_t)j * p.k_ss + 32 * db + lr] = dv[db][r];
           }
         }
@@ -381,7 +450,7 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       for (int r = 0; r < 16; ++r) {
         const int j = jw + 8 * (r >> 2) + 4 * g + (r & 3);
         if (j < p.Sk) {
-          DKg[(int64_t)j * p.k_ss + 32 * db + lr] = from_f32<T>(dk[db][r] * p.scale);
+          DKg[(int64_t)j * p.k_ss + 32 * db + lr] = from_f32<T>(dk[db][r] * dks);
           DVg[(int64_t)j * p.k_ss + 32 * db + lr] = from_f32<T>(dv[db][r]);
         }
       }
@@ -411,6 +480,9 @@ bool bwd_kv_split_eligible(const Params &p) {
   if (p.pse_kind == FA_PSE_DENSE) return false;
   if (p.pse_kind == FA_PSE_ALIBI && !(p.mask_flags & FA_MASK_CAUSAL)) return false;
   if (p.dpse) return false;
+  // the S accumulator's start value divides by scale * log2(e)
+  const float c = fabsf(p.scale_log2);
+  if (!(c > 1e-20f && c < 1e20f)) return false;
   return p.D == 64 || p.D == 128;
 }
 
