@@ -550,6 +550,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   const float c_log2 = p.scale_log2;
   const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
   const float sl2c = alibi ? sl2 / c_log2 : 0.f;
+  // Start values of the fast modes' accumulators (the lane's query is fixed):
+  // S starts at the ALiBi term of the element's key offset within its 32-key
+  // block in raw units (the block's own offset goes into the logit's offset),
+  // dP at -delta, so P is one fma and an exponential and dS one multiply.
+  f32x16 s_init, dp_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s_init[r] = sl2c * (float)(8 * (r >> 2) + (r & 3));
+    dp_init[r] = -dlt;
+  }
 
   int k_hi = p.Sk;
   if (causal) k_hi = min(k_hi, q0 + QBQ);
@@ -601,7 +611,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
       // one 32-key block at a time (LSE is known: no row max to wait for)
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s, dp;
+        if constexpr (GEN) {
+          s = dp = f32x16{};
+        } else {
+          s = s_init;
+          dp = dp_init;
+        }
         // fast steps: MFMA runs at raised issue priority, so the other wave on
         // the SIMD fills their gaps with its VALU work
         if (!GEN) __builtin_amdgcn_s_setprio(1);
@@ -624,14 +640,21 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
         // element r: key k0 + 32jb + 8(r/4) + 4g + r%4, query my_i
         if (!general) {
           const int lim = my_i - k0 - 4 * g;   // BAND: keys past the row have c > lim
+          const float offj = jb ? fmaf(32.f, sl2, off) : off;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 32 * jb + 8 * (r >> 2) + (r & 3);
-            float u = s[r];
-            if (alibi) u = fmaf(sl2c, (float)c, u);
-            float pr = exp2_fast(fmaf(u, c_log2, off));
+            float pr;
+            if constexpr (GEN) {
+              float u = s[r];
+              if (alibi) u = fmaf(sl2c, (float)c, u);
+              pr = exp2_fast(fmaf(u, c_log2, off));
+              dp[r] = dp[r] - dlt;
+            } else {
+              pr = exp2_fast(fmaf(s[r], c_log2, offj));   // S and dP carry their start values
+            }
             if (BAND) pr = c > lim ? 0.f : pr;
-            dp[r] = pr * (dp[r] - dlt);
+            dp[r] = pr * dp[r];
           }
         } else if constexpr (GEN) {
           // keys 4t .. 4t + 3 of a register group share one Philox call
