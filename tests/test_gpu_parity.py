@@ -120,6 +120,13 @@ for D in (32, 64, 128):
         SWEEP.append((2, 2, 70, 45, D, torch.float32, "BNSD", mask, _seed))
         _seed += 1
 SWEEP.append((2, 3, 33, 70, 64, torch.float32, "BSH", "causal+padding", _seed))
+_seed += 1
+# ALiBi without the causal rule, large enough for full tiles wholly below and
+# wholly above the diagonal (the forward's per-element fold on both sides)
+for D, dtype, layout in ((64, torch.bfloat16, "BNSD"), (128, torch.bfloat16, "BNSD"),
+                         (128, torch.float16, "BSH")):
+    SWEEP.append((1, 2, 600, 600, D, dtype, layout, "alibi", _seed))
+    _seed += 1
 
 
 @pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,seed", SWEEP,

@@ -81,7 +81,10 @@ enum : int { kFast = 0, kGeneral = 1, kDead = 2 };
 
 // DROP: dropout compiled in (keep_prob < 1); without it the kernel carries no
 // dropout code.
-template <typename T, int D, int NW, int RB_, int KBN_, bool DROP>
+// FOLD: ALiBi without the causal rule (fast tiles of both directions fold the
+// bias per element); the other problems run the FOLD = false instance, whose
+// fast tiles take the bias as the score accumulators' start value.
+template <typename T, int D, int NW, int RB_, int KBN_, bool DROP, bool FOLD>
 __global__ __launch_bounds__(NW * 64, (FwdCfg<T, D, NW, RB_, KBN_>::OCC))
 void fwd_mfma_kernel(Params p, int n_qtiles) {
   using C = FwdCfg<T, D, NW, RB_, KBN_>;
@@ -160,6 +163,11 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;   // slope in log2 units
   const float sl2c = alibi ? sl2 / c_log2 : 0.f;                 // slope in raw-score units
   const bool raw_ok = !alibi || c_log2 > 0.f;   // the fast forms fold sl2c into raw scores
+  // fast tiles: the ALiBi column term enters as the start value of the score
+  // accumulators (causal rule) or per element (fold_pe: ALiBi without it)
+  static_assert(KBN <= 2, "the exponentials' block offsets cover two 32-key blocks");
+  constexpr bool fold_pe = FOLD;   // the launcher sets FOLD = ALiBi without the causal rule
+  const float ash = alibi && !FOLD ? sl2c : 0.f;
   const bool f_pad = flags & FA_MASK_PADDING, f_mod = flags & FA_MASK_MODALITY;
   const bool f_exp = flags & FA_MASK_EXPLICIT;
 
@@ -277,11 +285,12 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 
   // S^T of one tile (two 32-key blocks) for every row block; operand reads
   // batched ahead of the MFMAs, each read feeding RB products
-  auto scores = [&](const uint16_t *ks, f32x16 (&s)[RB][KBN]) __attribute__((always_inline)) {
+  auto scores = [&](const uint16_t *ks, f32x16 (&s)[RB][KBN], const f32x16 &init)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int kb = 0; kb < KBN; ++kb) s[rb][kb] = f32x16{};
+      for (int kb = 0; kb < KBN; ++kb) s[rb][kb] = init;
 #pragma unroll
     for (int t0 = 0; t0 < KS; t0 += 4) {
       u32x4 ka[4][KBN];
@@ -383,7 +392,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 
     if (cls != kDead) {
       f32x16 s[RB][KBN];
-      scores(ks, s);
+      scores(ks, s, f32x16{});
       // logit of element r of block (rb, kb):  t = cs * s + lane_off[rb]  (base-2 units)
       float cs = c_log2, lane_off[RB], mx[RB];
 #pragma unroll
@@ -509,11 +518,17 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // all of them (-1), so the work can be spread over MFMA sections.  MASK
   // applies the causal rule per element (raw score -inf where key > row, which
   // needs c_log2 > 0); on a tile wholly below the diagonal it changes nothing.
+  // Under the causal rule every fast tile has direction +1, and the score
+  // accumulators start at the ALiBi term of the key's offset within its
+  // 32-key block (s_init; zero without ALiBi): the fold then only masks and
+  // takes the max, with the running max shifted by 32 ash at each 32-key
+  // block boundary and the exponentials offset by kb * 32 ash * c_log2.
+  // ALiBi without the causal rule folds the whole term per element.
   auto fold_max = [&](f32x16 (&sc)[RB][KBN], int k0, int part, float (&lane_off)[RB],
                       float (&mx)[RB], auto mask) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask)::value;
     const int adir = (causal || k0 + BN - 1 <= q0) ? 1 : -1;
-    const float a = alibi ? adir * sl2c : 0.f;
+    const float a = fold_pe ? adir * sl2c : 0.f;
     constexpr int NE = 16 * KBN;
     const int e0 = part < 0 ? 0 : part * NE / 4, e1 = part < 0 ? NE : (part + 1) * NE / 4;
 #pragma unroll
@@ -529,16 +544,22 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         if (e < e0 || e >= e1) continue;
         const int kb = e / 16, r = e % 16;
         const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-        const float v = fmaf(a, (float)c, sc[rb][kb][r]);
+        if (kb > 0 && r == 0) mx[rb] -= 32.f * ash;   // the block's values lack 32 kb ash
+        float v = sc[rb][kb][r];
+        if (fold_pe) v = fmaf(a, (float)c, v);
         sc[rb][kb][r] = (MASK && c > lim) ? -INFINITY : v;
         mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
       }
-      if (part < 0 || part == 3) mx[rb] = max_lane_pair(fmaf(mx[rb], c_log2, lane_off[rb]));
+      if (part < 0 || part == 3)
+        mx[rb] = max_lane_pair(fmaf(mx[rb] + (32.f * (KBN - 1)) * ash, c_log2, lane_off[rb]));
     }
   };
 
   f32x16 sA[RB][KBN], sB[RB][KBN];
   float loA[RB], mxA[RB], loB[RB], mxB[RB];
+  f32x16 s_init;   // formed here, after the generic phase, which does not use it
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s_init[r] = ash * (float)(8 * (r >> 2) + (r & 3));
   if (n_fast > 0) {
     const int f0 = ftile(0);
     load_tile(f0, K0, Kr);
@@ -547,7 +568,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   }
   vm_wait_barrier();
   if (n_fast > 0) {
-    scores(K0, sA);
+    scores(K0, sA, s_init);
     fold_max(sA, ftile(0) * BN, -1, loA, mxA, std::bool_constant<true>{});
   }
   lds_barrier();   // every wave is done with K0 before the first step refills it
@@ -567,10 +588,13 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     const int kt1 = (int)(pr & 0xffffu);
     if (n + 2 < n_fast) load_tile((int)(pr >> 16), B ? K1 : K0, Kr);
     if (n + 1 < n_fast) load_tile(kt1, B ? V0 : V1, Vr);
-    float alpha[RB], off[RB];
+    float alpha[RB], off[RB], offk[RB];
     update_max(mx, alpha);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) off[rb] = lo[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
+    for (int rb = 0; rb < RB; ++rb) {
+      off[rb] = lo[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
+      offk[rb] = fmaf(32.f * ash, c_log2, off[rb]);   // second 32-key block (KBN = 2)
+    }
 
     // Scores of tile n+1 interleaved with the exponentials of tile n, in an
     // order fixed by scheduling fences (only scalar work may cross them): the
@@ -597,7 +621,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int kb = 0; kb < KBN; ++kb) sn[rb][kb] = f32x16{};
+      for (int kb = 0; kb < KBN; ++kb) sn[rb][kb] = s_init;
       part[rb][0] = part[rb][1] = part[rb][2] = part[rb][3] = 0.f;
     }
     u32x4 va[NC][DB];
@@ -618,7 +642,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
       for (int e = t * EPS; e < (t + 1) * EPS; ++e) {
         const int rb = e / (16 * KBN), kb = (e / 16) % KBN, r = e % 16;
-        const float x = exp2_fast(fmaf(s[rb][kb][r], c_log2, off[rb]));
+        const float x = exp2_fast(fmaf(s[rb][kb][r], c_log2, kb ? offk[rb] : off[rb]));
         s[rb][kb][r] = x;
         part[rb][r & 3] += x;   // four short sum chains instead of one long one
       }
@@ -692,12 +716,16 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
   const int n_qtiles = (p.Sq + C::BM - 1) / C::BM;
   const int64_t blocks = (int64_t)n_qtiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
-  if (p.dropout)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN, true>), dim3((unsigned)blocks),
-                       dim3(C::NT), 0, s, p, n_qtiles);
-  else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, RB, KBN, false>), dim3((unsigned)blocks),
-                       dim3(C::NT), 0, s, p, n_qtiles);
+  const bool fold = p.pse_kind == FA_PSE_ALIBI && !(p.mask_flags & FA_MASK_CAUSAL);
+  const dim3 grid((unsigned)blocks), block(C::NT);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, p, n_qtiles); };
+  if (p.dropout) {
+    if (fold) go(fwd_mfma_kernel<T, D, NW, RB, KBN, true, true>);
+    else go(fwd_mfma_kernel<T, D, NW, RB, KBN, true, false>);
+  } else {
+    if (fold) go(fwd_mfma_kernel<T, D, NW, RB, KBN, false, true>);
+    else go(fwd_mfma_kernel<T, D, NW, RB, KBN, false, false>);
+  }
   return hipGetLastError();
 }
 
