@@ -139,10 +139,14 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     tile_offsets<D, SQB, NPW>(voff, qrow_b, w, l);
     // block n's Q / dO tiles and statistics into ring slot bi (wave w loads
     // its share of the tiles and 16 rows of LSE (w < 2) or delta (w >= 2))
-    auto load_block = [&](int n, auto bi) __attribute__((always_inline)) {
+    auto load_tiles = [&](int n, auto bi) __attribute__((always_inline)) {
       const int i0 = (it_begin + n) * SQB;
       tile_load<D, SQB, NPW>(qbuf(bi), Qr, voff, (uint32_t)i0 * qrow_b, w);
       tile_load<D, SQB, NPW>(gbuf(bi), Gr, voff, (uint32_t)i0 * qrow_b, w);
+    };
+    // (rows past S_q read as zeros, so a block past the last one is harmless)
+    auto load_stats = [&](int n, auto bi) __attribute__((always_inline)) {
+      const int i0 = (it_begin + n) * SQB;
       float *sd = (w < 2 ? lbuf(bi) : ebuf(bi)) + 16 * (w & 1);
       if (l < 16) stats_load(sd, Sr, 4u * (uint32_t)l, 4u * (uint32_t)(i0 + 16 * (w & 1)));
     };
@@ -152,26 +156,19 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     for (int t = 0; t < KS; ++t) ro[t] = row_off<D>(lr, 2 * t + g);
     const float c_log2 = p.scale_log2;
     const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
-    // The S accumulator of element r (query i = i0 + 4g + c, c = 8(r/4) + r%4)
-    // starts at u = -(LSE_i log2e + slope log2e c) / c_log2, so that
-    // c_log2 (S + u) + slope log2e (my_j - i0 - 4g) is the base-2 logit
-    // c_log2 S + slope log2e (my_j - i) - LSE_i log2e with one fma per
-    // element; the per-element constants live in scalar registers.
-    const float inv_c = 1.f / c_log2;
-    const float kA = -kLog2e * inv_c;
-    float cu[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      cu[r] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                            int, -sl2 * inv_c * (float)(8 * (r >> 2) + (r & 3)))));
+    // The S accumulator of row i (block start i0) starts at the row term
+    // W_i = -(LSE_i log2e + slope log2e (i - i0)) / c_log2, which a consumer
+    // wave writes over the block's LSE in LDS two steps ahead, so that
+    // c_log2 (S + W_i) + slope log2e (my_j - i0) is the base-2 logit
+    // c_log2 S + slope log2e (my_j - i) - LSE_i log2e: one fma per element.
     // start values of block bi's S and dP accumulators
     auto init_acc = [&](auto bi, f32x16 &s0, f32x16 &dp0) __attribute__((always_inline)) {
       const float *ls = lbuf(bi), *ds = ebuf(bi);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 lv = *(const f32x4 *)&ls[8 * rr + 4 * g];
+        const f32x4 wv4 = *(const f32x4 *)&ls[8 * rr + 4 * g];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s0[4 * rr + q] = fmaf(lv[q], kA, cu[4 * rr + q]);
+        for (int q = 0; q < 4; ++q) s0[4 * rr + q] = wv4[q];
       }
       if constexpr (DROP) {
         dp0 = f32x16{};
@@ -242,21 +239,25 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       const uint16_t *qn = qbuf(BufIdx<(B + 1) % NSL>{}), *gn = gbuf(BufIdx<(B + 1) % NSL>{});
       const float *ds = ebuf(bi);
       const int i0 = (it_begin + n) * SQB;
-      const float L = sl2 * (float)(my_j - i0 - 4 * g);
+      const float L = sl2 * (float)(my_j - i0);
       const int lim = causal ? my_j - i0 - 4 * g : INT_MIN;   // c < lim is hidden
       // dropout: the four lanes of a quad hold four consecutive keys and the
       // same 16 queries, so lane q of the quad draws the Philox words of the
       // queries with r % 4 == q (one call covers the quad's four keys), packs
       // the keep bits, and the quad exchanges them; bit 4 rr of kq[q] is then
       // the keep bit of element 4 rr + q for this lane's key
-      // LDS reads first, all in flight together: block n+1's LSE (for the S
+      // LDS reads first, all in flight together: block n+1's row terms (the S
       // start values) and delta (the dP start values), its first KPF operand
       // k-steps, and under dropout block n's delta
-      f32x4 lvr[4], dl[4];
+      f32x4 dl[4];
       {
         const float *ln = lbuf(BufIdx<(B + 1) % NSL>{}), *dn = ebuf(BufIdx<(B + 1) % NSL>{});
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) lvr[rr] = *(const f32x4 *)&ln[8 * rr + 4 * g];
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 wv4 = *(const f32x4 *)&ln[8 * rr + 4 * g];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sn[4 * rr + q] = wv4[q];
+        }
         if constexpr (DROP) {
           dpn = f32x16{};
 #pragma unroll
@@ -315,11 +316,6 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       for (int r = 0; r < PRE; ++r) elem(r);
       __builtin_amdgcn_sched_barrier(0x0004);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sn[4 * rr + q] = fmaf(lvr[rr][q], kA, cu[4 * rr + q]);
-      __builtin_amdgcn_sched_barrier(0x0004);
-#pragma unroll
       for (int t = 0; t < KS; ++t) {
         if (t + KPF < KS) {
           qa[t + KPF] = read_row_at<D>(qn, 0, ro[t + KPF]);
@@ -338,13 +334,21 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
       x[192] = pack8<T>(dp, 8);
       __builtin_amdgcn_sched_barrier(0);
       const bool more = n + 3 < nb;
-      if (more) load_block(n + 3, BufIdx<(B + 3) % NSL>{});
+      if (more) {
+        load_tiles(n + 3, BufIdx<(B + 3) % NSL>{});
+        load_stats(n + 4, BufIdx<(B + 4) % NSL>{});
+      }
       finish(more);
     };
-    if (nb > 0) load_block(0, BufIdx<0>{});
-    if (nb > 1) load_block(1, BufIdx<1>{});
-    if (nb > 2) load_block(2, BufIdx<2>{});
-    finish(nb > 2);   // blocks 0 and 1 have landed
+    if (nb > 0) load_tiles(0, BufIdx<0>{});
+    if (nb > 1) load_tiles(1, BufIdx<1>{});
+    if (nb > 2) load_tiles(2, BufIdx<2>{});
+    load_stats(0, BufIdx<0>{});
+    load_stats(1, BufIdx<1>{});
+    load_stats(2, BufIdx<2>{});
+    load_stats(3, BufIdx<3>{});
+    finish(false);   // everything has landed; the consumers turn the LSE of
+    finish(false);   // blocks 0 and 1 into row terms between these barriers
     f32x16 sA, dpA, sB, dpB;
     scores(BufIdx<0>{}, sA, dpA);   // stale when nb == 0, and unused
     const std::true_type band;
@@ -405,15 +409,32 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
     };
     // step n: consume block n-1 (exchange slot (n-1)%2, operands already in
     // registers), then read block n's operands from ring slot n % 6
+    // the producers' S start values: block bi's LSE (landed) becomes the row
+    // term W_i = -(LSE_i log2e + slope log2e (i - i0)) / c_log2 in place
+    const float inv_c = 1.f / p.scale_log2;
+    const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;
+    auto row_terms = [&](auto bi) __attribute__((always_inline)) {
+      if (l < SQB) {
+        float *ls = lbuf(bi);
+        ls[l] = -fmaf(ls[l], kLog2e, sl2 * (float)l) * inv_c;
+      }
+    };
+    // step n: besides, the first consumer wave writes the row terms of block
+    // n+2 (its statistics landed by the end of step n-1; the producers read
+    // them in step n+1)
     auto cstep = [&](int n, auto bi) __attribute__((always_inline)) {
       constexpr int B = decltype(bi)::value;
       opaque(to);
       if (n >= 1 && n - 1 < nb) consume(BufIdx<(B + NSL - 1) % NSL>{});
       __builtin_amdgcn_sched_barrier(0);
       if (n < nb) prefetch(bi);
+      if (wv == NPW) row_terms(BufIdx<(B + 2) % NSL>{});
       finish();
     };
-    finish();   // the producers' set-up barrier
+    finish();   // the producers' loads of the first blocks have landed
+    if (wv == NPW) row_terms(BufIdx<0>{});
+    if (wv == NPW + 1) row_terms(BufIdx<1>{});
+    finish();
     for (int n = 0; n <= nb; n += NSL) {
       cstep(n, BufIdx<0>{});
       if (n + 1 <= nb) cstep(n + 1, BufIdx<1>{});
