@@ -601,7 +601,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
     // accumulation stays unconditional
     // (the fast ALiBi form folds slope / c_log2 into raw scores: c_log2 > 0)
-    bool general = f_elem || dense || DROP || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
+    // (in the general phase dropout keeps every tile on the per-element code,
+    // whose fast-tile branch draws no keep mask)
+    bool general = f_elem || dense || (GEN && DROP) || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
                    (alibi && !(c_log2 > 0.f));
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
@@ -616,7 +618,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
           s = dp = f32x16{};
         } else {
           s = s_init;
-          dp = dp_init;
+          if constexpr (DROP) dp = f32x16{};   // the keep mask scales dP before delta
+          else dp = dp_init;
         }
         // fast steps: MFMA runs at raised issue priority, so the other wave on
         // the SIMD fills their gaps with its VALU work
@@ -641,6 +644,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
         if (!general) {
           const int lim = my_i - k0 - 4 * g;   // BAND: keys past the row have c > lim
           const float offj = jb ? fmaf(32.f, sl2, off) : off;
+          // dropout: keys 4t .. 4t + 3 of a register group share one Philox call
+          uint32_t keep[4] = {0u, 0u, 0u, 0u};
+          if constexpr (DROP && !GEN) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              keep[rr] = dropout_keep4(p, b, h, my_i, k0 + 32 * jb + 8 * rr + 4 * g);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 32 * jb + 8 * (r >> 2) + (r & 3);
@@ -651,7 +661,11 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
               pr = exp2_fast(fmaf(u, c_log2, off));
               dp[r] = dp[r] - dlt;
             } else {
-              pr = exp2_fast(fmaf(s[r], c_log2, offj));   // S and dP carry their start values
+              pr = exp2_fast(fmaf(s[r], c_log2, offj));   // S carries its start value
+              if constexpr (DROP) {
+                const float m = dropout_scale(p, (keep[r >> 2] >> (r & 3)) & 1u);
+                dp[r] = dp[r] * m - dlt;   // dropout masks dP like P
+              }
             }
             if (BAND) pr = c > lim ? 0.f : pr;
             dp[r] = pr * dp[r];
@@ -699,13 +713,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   };
 
   // fast range [0, f_end): full tiles every row of the workgroup sees whole
-  // (below the causal diagonal; ALiBi direction +1), without mask tensors,
-  // dense bias or dropout.  Under the causal rule alone the full tiles on the
+  // (below the causal diagonal; ALiBi direction +1), without mask tensors or
+  // dense bias.  Under the causal rule alone the full tiles on the
   // diagonal, [f_end, b_end), run the fast code with the causal mask (it needs
   // c_log2 > 0); the rest, [b_end, kt_end), take the general code.  Those two
   // groups go first, one per step.
   int f_end = 0, b_end = 0;
-  if (!f_elem && !dense && !DROP && q0 + QBQ <= p.Sq && (!alibi || c_log2 > 0.f)) {
+  if (!f_elem && !dense && q0 + QBQ <= p.Sq && (!alibi || c_log2 > 0.f)) {
     f_end = min(kt_end, p.Sk / KBQ);
     b_end = f_end;
     if (causal || alibi) f_end = min(f_end, (q0 + 1) / KBQ);
