@@ -147,6 +147,14 @@ def test_fp8_scale_zero_with_alibi():
     check_fp8(pr, t8, sc, o, lse)
 
 
+def test_fp8_tiny_scale_with_alibi():
+    """A scale so small that slope / c could overflow: the per-element path."""
+    pr, t8, sc = make_fp8_case(1, 2, 300, 300, 128, "BNSD", "causal+alibi", 3975)
+    pr.scale = 1e-38
+    o, lse = run_fp8(pr, t8, sc)
+    check_fp8(pr, t8, sc, o, lse)
+
+
 def test_fp8_no_keys_and_repeatable():
     pr, t8, sc = make_fp8_case(1, 2, 40, 0, 128, "BNSD", "none", 3950)
     o, lse = run_fp8(pr, t8, sc)

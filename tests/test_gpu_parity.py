@@ -232,6 +232,20 @@ def test_scale_zero(mask):
     check_bwd(pr, o, lse)
 
 
+@pytest.mark.parametrize("scale", [1e-38, 1e-12])
+@pytest.mark.parametrize("mask", ["alibi", "causal+alibi"])
+def test_tiny_scale(mask, scale):
+    """A positive scale small enough that slope / (scale log2 e) overflows
+    (1e-38: slope / c near 1e38, past the float range once multiplied by a key
+    offset) sends the ALiBi tiles to the per-element path; at 1e-12 the
+    raw-unit forms run with slope / c near 1e12.  Either way the logits are the
+    bias plus a negligible score term."""
+    pr = make_case(1, 2, 300, 300, 128, torch.bfloat16, "BNSD", mask, 975)
+    pr.scale = scale
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_large_scores_exercise_running_max(D):
     pr = make_case(1, 2, 300, 300, D, torch.bfloat16, "BNSD", "causal", 904 + D)

@@ -600,11 +600,11 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     // fast or general tile; tiles hidden from this wave (at most one per
     // workgroup on the causal diagonal) take the general path (dS = 0) so the
     // accumulation stays unconditional
-    // (the fast ALiBi form folds slope / c_log2 into raw scores: c_log2 > 0)
+    // (the fast ALiBi form folds slope / c_log2 into raw scores: c_log2 > kRawMinC)
     // (in the general phase dropout keeps every tile on the per-element code,
     // whose fast-tile branch draws no keep mask)
     bool general = f_elem || dense || (GEN && DROP) || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
-                   (alibi && !(c_log2 > 0.f));
+                   (alibi && !(c_log2 > kRawMinC));
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
     if (!GEN) general = false;   // the fast phase only visits tiles fast for every wave
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
   // c_log2 > 0); the rest, [b_end, kt_end), take the general code.  Those two
   // groups go first, one per step.
   int f_end = 0, b_end = 0;
-  if (!f_elem && !dense && q0 + QBQ <= p.Sq && (!alibi || c_log2 > 0.f)) {
+  if (!f_elem && !dense && q0 + QBQ <= p.Sq && (!alibi || c_log2 > kRawMinC)) {
     f_end = min(kt_end, p.Sk / KBQ);
     b_end = f_end;
     if (causal || alibi) f_end = min(f_end, (q0 + 1) / KBQ);

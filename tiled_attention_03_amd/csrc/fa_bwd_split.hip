@@ -503,7 +503,7 @@ bool bwd_kv_split_eligible(const Params &p) {
   if (p.dpse) return false;
   // the S accumulator's start value divides by scale * log2(e)
   const float c = fabsf(p.scale_log2);
-  if (!(c > 1e-20f && c < 1e20f)) return false;
+  if (!(c > kRawMinC && c < 1e20f)) return false;
   return p.D == 64 || p.D == 128;
 }
 

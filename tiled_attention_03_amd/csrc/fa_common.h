@@ -21,6 +21,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The raw-unit ALiBi forms divide the slope by c_log2 = scale * log2(e); at
+// or below this c_log2 that quotient could overflow, and the tiles take the
+// per-element path instead.
+constexpr float kRawMinC = 1e-20f;
 
 struct Params {
   // tensors (device pointers)

@@ -162,7 +162,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   const float c_log2 = p.scale_log2;
   const float sl2 = alibi ? p.alibi_slopes[h] * kLog2e : 0.f;   // slope in log2 units
   const float sl2c = alibi ? sl2 / c_log2 : 0.f;                 // slope in raw-score units
-  const bool raw_ok = !alibi || c_log2 > 0.f;   // the fast forms fold sl2c into raw scores
+  const bool raw_ok = !alibi || c_log2 > kRawMinC;   // the fast forms fold sl2c into raw scores
   // fast tiles: the ALiBi column term enters as the start value of the score
   // accumulators (causal rule) or per element (fold_pe: ALiBi without it)
   static_assert(KBN <= 2, "the exponentials' block offsets cover two 32-key blocks");

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(Params p, int n_qti
   // Only without mask tensors and dense bias; the other tiles run `step`.
   int f_end = kt_begin;
   // (the fast form folds slope / c into raw scores, which needs c > 0)
-  if (!dense && !f_exp && !f_pad && !f_mod && (!alibi || c_log2 > 0.f)) {
+  if (!dense && !f_exp && !f_pad && !f_mod && (!alibi || c_log2 > kRawMinC)) {
     f_end = min(kt_end, p.Sk / kBN);                          // full tiles
     if (causal || alibi) f_end = min(f_end, (q0 + 1) / kBN);   // k0 + 63 <= q0
     f_end = max(f_end, kt_begin);
