@@ -340,6 +340,11 @@ for mask, kp in (("explicit", 0.7), ("modality+diag", 0.9), ("dense", 0.75),
     DROP.append((2, 2, 160, 96, 128, torch.bfloat16, "BSH", mask, kp, _dseed))
     _dseed += 1
 DROP.append((1, 2, 1024, 1024, 128, torch.bfloat16, "BNSD", "causal+alibi", 0.9, _dseed))
+_dseed += 1
+# the BSH layout through the fast (pipelined) dropout paths
+DROP.append((1, 3, 384, 384, 128, torch.float16, "BSH", "causal", 0.7, _dseed))
+_dseed += 1
+DROP.append((2, 2, 320, 320, 64, torch.bfloat16, "BSH", "none", 0.85, _dseed))
 
 
 @pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,kp,seed", DROP,
