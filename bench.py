@@ -281,6 +281,90 @@ def bench_maxsim(args):
     print(json.dumps(rec), flush=True)
 
 
+def attention_bytes(pr) -> int:
+    """Bytes the forward result depends on: every query row, the key and value
+    rows some query may see (valid keys only under a padding mask), the masks,
+    and the outputs O and LSE."""
+    es = pr.q.element_size()
+    D, H, B = pr.head_dim, pr.heads, pr.batch
+    q_bytes = B * H * pr.seq_q * D * es
+    if pr.key_valid is not None:
+        kv_rows = int(pr.key_valid.sum()) * H
+    else:
+        kv_rows = B * H * pr.seq_k
+    mask_bytes = 0
+    if pr.key_valid is not None:
+        mask_bytes += pr.key_valid.numel()
+    if pr.q_modality is not None:
+        mask_bytes += pr.q_modality.numel() + pr.k_modality.numel()
+    return q_bytes + 2 * kv_rows * D * es + mask_bytes + q_bytes + B * H * pr.seq_q * 4
+
+
+def bench_config(cid: int, steps: int, warmup: int) -> dict:
+    """Forward (and, for information, backward) times of one more workload:
+    HIP events around each call on the call's stream; warm = the same tensors
+    every call, cold = calls alternating between two tensor sets."""
+    import torch
+    from tiled_attention_03_amd import binding as fa
+    from tiled_attention_03_amd import inputs
+
+    dev = "cuda:0"
+    pr = inputs.config(cid)
+    kw = fa.problem_kwargs(pr, dev)
+    sets = []
+    for _ in range(2):
+        q, k, v, do = (t.to(dev) for t in (pr.q, pr.k, pr.v, pr.do))
+        o = torch.empty_like(q)
+        lse = torch.empty(pr.batch, pr.heads, pr.seq_q, dtype=torch.float32, device=dev)
+        sets.append((q, k, v, do, o, lse, torch.empty_like(q), torch.empty_like(k),
+                     torch.empty_like(v)))
+    plan = fa.Plan(sets[0][0], sets[0][1], heads=pr.heads, layout=pr.layout, **kw)
+
+    def fwd(t):
+        plan.fwd(t[0], t[1], t[2], t[4], t[5])
+
+    def bwd(t):
+        plan.bwd_prep(t[4], t[3])
+        plan.bwd_main(t[0], t[1], t[2], t[5], t[3], t[7], t[8])
+        plan.bwd_post(t[0], t[1], t[2], t[5], t[3], t[6])
+
+    def timed(fn, alternate):
+        for i in range(warmup):
+            fn(sets[i % 2] if alternate else sets[0])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (e0, e1) in enumerate(evs):
+            t = sets[i % 2] if alternate else sets[0]
+            e0.record()
+            fn(t)
+            e1.record()
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return ts[len(ts) // 2]
+
+    fwd_warm, fwd_cold = timed(fwd, False), timed(fwd, True)
+    for t in sets:
+        fwd(t)
+    bwd_warm = timed(bwd, False)
+    pairs = visible_pairs(pr)
+    D = pr.head_dim
+    f_fwd, f_bwd = 4 * D * pairs, 10 * D * pairs
+    nbytes = attention_bytes(pr)
+    rec = {"workload": pr.name, "visible_pairs": pairs, "median_of": steps,
+           "fwd_ms_warm": round(fwd_warm, 5), "fwd_ms_cold": round(fwd_cold, 5),
+           "fwd_tflops": round(f_fwd / (fwd_warm * 1e-3) / 1e12, 2),
+           "fwd_pct_of_bf16_peak": round(100 * f_fwd / (fwd_warm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "fwd_bytes": nbytes,
+           "fwd_gbs_cold": round(nbytes / (fwd_cold * 1e-3) / 1e9, 1),
+           "fwd_pct_of_hbm_cold": round(100 * nbytes / (fwd_cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "bwd_ms_warm": round(bwd_warm, 5),
+           "bwd_tflops": round(f_bwd / (bwd_warm * 1e-3) / 1e12, 2)}
+    del sets, plan
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +373,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--more", default="2,3,4",
+                    help="comma-separated workload ids whose forward is also timed and reported "
+                         "under 'workloads' (empty: none)")
     ap.add_argument("--keep-prob", type=float, default=1.0,
                     help="dropout keep probability (1.0 = no dropout, the headline workload)")
     ap.add_argument("--dropout-seed", type=int, default=0x5EED)
@@ -441,6 +528,8 @@ def main():
         "kernel_tflops": {n: round(FLOPS_PER_PAIR_D[n] * D * pairs / (per[n] * 1e-3) / 1e12, 2)
                           for n in names if FLOPS_PER_PAIR_D[n]},
     }
+    if args.more:
+        rec["workloads"] = {f"c{c}": bench_config(int(c), 50, 10) for c in args.more.split(",") if c}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pr, heads=args.cpu_heads) if args.config == 5 else None
     print(json.dumps(rec), flush=True)

@@ -210,3 +210,88 @@ def test_fp8_entry_points_validate():
     # empty problems need nothing
     assert fa.lib.fa_fwd_fp8(ctypes.byref(base_problem(dtype=fa.FA_FP8_E4M3, batch=0)), None, None,
                              None, 1.0, 1.0, 1.0, None, None, None, 0, None) == 0
+
+
+# ----------------------------------------------------------------------------------
+# the Python binding's checks: each raises before any pointer reaches the library
+
+def _t(*shape, dtype=None, device="cpu"):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16, device=device)
+
+
+def test_binding_requires_an_explicit_scale():
+    q, k = _t(1, 2, 8, 64), _t(1, 2, 8, 64)
+    with pytest.raises(TypeError, match="scale"):
+        fa.make_problem(q, k, heads=2)
+    p, _ = fa.make_problem(q, k, heads=2, scale=0.25)
+    assert abs(p.scale - 0.25) < 1e-12
+
+
+@pytest.mark.parametrize("field", ["key_valid", "alibi_slopes", "explicit_mask", "pse",
+                                   "q_modality"])
+def test_binding_rejects_masks_on_another_device(field):
+    import torch
+    q, k = _t(1, 2, 8, 64), _t(1, 2, 8, 64)
+    kw = {"key_valid": dict(key_valid=_t(1, 8, dtype=torch.bool, device="meta")),
+          "alibi_slopes": dict(alibi_slopes=_t(2, dtype=torch.float32, device="meta")),
+          "explicit_mask": dict(explicit_mask=_t(1, 1, 8, 8, dtype=torch.bool, device="meta")),
+          "pse": dict(pse=_t(1, 2, 8, 8, dtype=torch.float32, device="meta")),
+          "q_modality": dict(q_modality=_t(1, 8, dtype=torch.int8, device="meta"),
+                             k_modality=_t(1, 8, dtype=torch.int8, device="meta"),
+                             modality_allow=[[1, 1], [0, 1]])}[field]
+    with pytest.raises(ValueError, match="device"):
+        fa.make_problem(q, k, heads=2, scale=0.125, **kw)
+
+
+def test_binding_rejects_partial_modality_arguments():
+    import torch
+    q, k = _t(1, 2, 8, 64), _t(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="modality"):
+        fa.make_problem(q, k, heads=2, scale=0.125, q_modality=_t(1, 8, dtype=torch.int8))
+
+
+@pytest.mark.parametrize("bad", ["v_shape", "o_dtype", "do_shape", "lse_dtype", "lse_shape"])
+def test_binding_backward_checks_shapes_and_dtypes(bad):
+    import torch
+    B, H, S, D = 1, 2, 8, 64
+    q, k, v, o, do = (_t(B, H, S, D) for _ in range(5))
+    lse = _t(B, H, S, dtype=torch.float32)
+    if bad == "v_shape":
+        v = _t(B, H, S + 1, D)
+    elif bad == "o_dtype":
+        o = _t(B, H, S, D, dtype=torch.float16)
+    elif bad == "do_shape":
+        do = _t(B, H, S - 1, D)
+    elif bad == "lse_dtype":
+        lse = _t(B, H, S, dtype=torch.bfloat16)
+    else:
+        lse = _t(B, H, S + 2, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fa.bwd(q, k, v, o, lse, do, heads=H, scale=0.125)
+
+
+@pytest.mark.parametrize("bad", ["v_dtype", "out_shape", "lse_shape"])
+def test_binding_forward_checks_outputs(bad):
+    import torch
+    B, H, S, D = 1, 2, 8, 64
+    q, k, v = _t(B, H, S, D), _t(B, H, S, D), _t(B, H, S, D)
+    kw = {}
+    if bad == "v_dtype":
+        v = _t(B, H, S, D, dtype=torch.float16)
+    elif bad == "out_shape":
+        kw["out"] = _t(B, H, S - 1, D)
+    else:
+        kw["lse"] = _t(B, H, S, 1, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k, v, heads=H, scale=0.125, **kw)
+
+
+def test_long_key_ranges_are_accepted():
+    """The forward walks key tiles in chunks, so S_k past the size of one chunk's
+    tile list (256 tiles of 64 keys) is a supported problem: validation passes and
+    the call goes on to the pointer checks."""
+    p = base_problem(seq_k=70000, mask_flags=fa.FA_MASK_PADDING)
+    assert call_fwd(p) == fa.FA_ERR_INVALID_ARG           # key_valid missing: pointer check
+    p.key_valid = 1 << 20
+    assert call_fwd(p, q=None) == fa.FA_ERR_INVALID_ARG   # reached the tensor checks

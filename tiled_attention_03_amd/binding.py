@@ -8,7 +8,6 @@ device-memory plumbing).  If ``libfa.so`` is missing it raises at import.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -172,14 +171,27 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
         H, D = heads, HD // heads
         if tuple(k.shape) != (B, Sk, HD):
             raise ValueError("k must be [B, S_k, H*D] with q's B and hidden size")
+    if scale is None:
+        raise TypeError("scale is required (the operator has no default; 1/sqrt(D) is usual)")
+    if k.device != q.device:
+        raise ValueError("q and k must be on one device")
     p = FaProblem()
     p.batch, p.head_num, p.seq_q, p.seq_k, p.head_dim = B, H, Sq, Sk, D
     p.layout = _LAYOUTS[layout]
     p.dtype = _DTYPES[q.dtype]
-    p.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    p.scale = float(scale)
     p.keep_prob = float(keep_prob)
     p.dropout_seed = int(dropout_seed) & 0xFFFFFFFFFFFFFFFF
     p.grad_f32 = int(bool(grad_f32))
+
+    def on_dev(t, what):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{what} must be on q's device ({q.device}), not {t.device}")
+
+    for t, what in ((explicit_mask, "explicit_mask"), (q_modality, "q_modality"),
+                    (k_modality, "k_modality"), (key_valid, "key_valid"),
+                    (alibi_slopes, "alibi_slopes"), (pse, "pse"), (dpse, "dpse")):
+        on_dev(t, what)
     if dpse is not None:
         if dpse.dtype != torch.float32 or tuple(dpse.shape) != (B, H, Sq, Sk) or \
                 not dpse.is_contiguous():
@@ -206,6 +218,9 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, *, heads: int, layout: str = 
         p.em_stride_h = em.stride(1) if em.shape[1] > 1 else 0
         p.em_stride_q = em.stride(2)
         keep.append(em)
+    if (q_modality is None) != (k_modality is None) or \
+            (q_modality is not None and modality_allow is None):
+        raise ValueError("a modality mask needs q_modality, k_modality and modality_allow")
     if q_modality is not None:
         qm = q_modality.to(torch.int8).contiguous()
         km = k_modality.to(torch.int8).contiguous()
@@ -279,15 +294,28 @@ def _lse_shape(p: FaProblem):
     return (p.batch, p.head_num, p.seq_q)
 
 
+def _same(t, like, dtype, device, what):
+    """``t`` must have ``like``'s shape, ``dtype`` and ``device``."""
+    if tuple(t.shape) != tuple(like.shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{what} must be {dtype} of shape {tuple(like.shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _lse_ok(lse, p: FaProblem, device):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != _lse_shape(p) or lse.device != device:
+        raise ValueError(f"lse must be float32 of shape {_lse_shape(p)} on {device}")
+
+
 def fwd(q, k, v, *, heads: int, layout: str = "BNSD", out=None, lse=None, **kw):
     """O, LSE = attention(q, k, v).  ``kw`` are the mask/bias arguments of
     :func:`make_problem`.  Returns (O in q's layout and dtype, LSE float32 [B,H,S_q])."""
-    _contig(q, k, v)
+    _contig(q, k, v, out, lse)
     p, keep = make_problem(q, k, heads=heads, layout=layout, **kw)
-    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
-        raise ValueError("v must match k's shape and q's dtype")
+    _same(v, k, q.dtype, q.device, "v")
     o = torch.empty_like(q) if out is None else out
     l = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device) if lse is None else lse
+    _same(o, q, q.dtype, q.device, "out")
+    _lse_ok(l, p, q.device)
     _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _stream()),
            "fa_fwd")
     return o, l
@@ -299,8 +327,7 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, *, he
     returns (O bf16 in q's layout, LSE float32 [B,H,S_q])."""
     _contig(q, k, v)
     p, keep = make_problem(q, k, heads=heads, layout=layout, **kw)
-    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
-        raise ValueError("v must match k's shape and q's dtype")
+    _same(v, k, q.dtype, q.device, "v")
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     l = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -328,19 +355,25 @@ def bwd(q, k, v, o, lse, do, *, heads: int, layout: str = "BNSD", workspace=None
     buffer, float32 [B, H, S_q, S_k]) the bias gradient is written and
     returned as a fourth value."""
     _contig(q, k, v, o, lse, do)
+    _same(v, k, q.dtype, q.device, "v")
+    _same(o, q, q.dtype, q.device, "o")
+    _same(do, q, q.dtype, q.device, "do")
     if want_dpse and dpse is None:
         B = q.shape[0]
         Sq, Sk = (q.shape[2], k.shape[2]) if layout == "BNSD" else (q.shape[1], k.shape[1])
         dpse = torch.empty(B, heads, Sq, Sk, dtype=torch.float32, device=q.device)
     p, keep = make_problem(q, k, heads=heads, layout=layout, dpse=dpse, **kw)
+    _lse_ok(lse, p, q.device)
     n = ctypes.c_size_t(0)
     _check(lib.fa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)), "fa_bwd_workspace_size")
+    if workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     ws = workspace if workspace is not None else torch.empty(max(n.value, 256), dtype=torch.uint8,
                                                              device=q.device)
     gdt = torch.float32 if p.grad_f32 else q.dtype
     dq, dk, dv = (torch.empty(t.shape, dtype=gdt, device=t.device) for t in (q, k, v))
     _check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()), "fa_bwd")
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream()), "fa_bwd")
     return (dq, dk, dv) if dpse is None else (dq, dk, dv, dpse)
 
 

@@ -9,8 +9,12 @@
 
 namespace fa {
 
-// Forward, bf16/f16 MFMA path (D = 64 or 128).
+// Forward, bf16/f16 MFMA path (D = 64 or 128), and its per-(dtype, D) instances.
 hipError_t launch_fwd_mfma(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_fwd_bf16_d64(const Params &p, hipStream_t s);
+hipError_t launch_fwd_bf16_d128(const Params &p, hipStream_t s);
+hipError_t launch_fwd_f16_d64(const Params &p, hipStream_t s);
+hipError_t launch_fwd_f16_d128(const Params &p, hipStream_t s);
 // Forward, fp8 (OCP e4m3) inputs, D = 64 or 128: a pre-pass writes the
 // permuted V^T tiles into p.vt, then the MFMA kernel; O is bf16.
 hipError_t launch_fwd_fp8(const Params &p, hipStream_t s);
