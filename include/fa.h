@@ -20,7 +20,8 @@
  * and bias arrays inside fa_problem) are DEVICE pointers owned by the caller.
  * The fa_problem struct itself is host memory read only during the call.
  * The library allocates no device memory; the backward takes a caller
- * workspace of fa_bwd_workspace_size() bytes.
+ * workspace of fa_bwd_workspace_size() bytes (fa_bwd_noalloc instead uses a
+ * fixed device array inside the library).
  *
  * Layouts (element strides; the last dimension is contiguous):
  *   FA_BNSD: Q/O/dO/dQ [B, H, S_q, D]; K/V/dK/dV [B, H, S_k, D].
@@ -109,7 +110,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_OK = 0,
@@ -195,6 +196,24 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
                  const void *o, const float *lse, const void *dout,
                  void *dq, void *dk, void *dv,
                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs and errors as fa_bwd minus the
+ * workspace: the row terms D_i live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, held until
+ * the process ends), so the problem must satisfy
+ * 4 * B * H * S_q <= FA_NOALLOC_SCRATCH_BYTES (rounded up to 256 bytes),
+ * else FA_ERR_WORKSPACE, before any launch.  The call allocates nothing.
+ * The stream must belong to the current device; the array's address there is
+ * looked up once per device (FA_ERR_HIP if that fails).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * host threads) race and give wrong gradients; calls ordered on one stream do
+ * not.  The array needs no clearing: each call writes the row terms it reads. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa_status fa_bwd_noalloc(const fa_problem *p, const void *q, const void *k, const void *v,
+                         const void *o, const float *lse, const void *dout,
+                         void *dq, void *dk, void *dv, hipStream_t stream);
 
 /* Backward step 1: row terms D_i = sum_d dO_id * O_id into the workspace. */
 fa_status fa_bwd_prep(const fa_problem *p, const void *o, const void *dout,

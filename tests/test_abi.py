@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.abi_version() == 5
+    assert fa.abi_version() == 6
     assert fa.status_str(0) == "ok"
     assert fa.status_str(-2) == "unsupported configuration"
 
@@ -295,3 +295,18 @@ def test_long_key_ranges_are_accepted():
     assert call_fwd(p) == fa.FA_ERR_INVALID_ARG           # key_valid missing: pointer check
     p.key_valid = 1 << 20
     assert call_fwd(p, q=None) == fa.FA_ERR_INVALID_ARG   # reached the tensor checks
+
+
+def test_noalloc_backward_rejects_problems_past_its_scratch():
+    """fa_bwd_noalloc keeps the row terms (4 bytes per query row of every head) in
+    a fixed 16 MiB device array: a larger problem is refused before any launch."""
+    def call(p):
+        return fa.lib.fa_bwd_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, None)
+    assert call(base_problem(batch=1, head_num=64, seq_q=70000, seq_k=64)) == fa.FA_ERR_WORKSPACE
+    assert call(base_problem(keep_prob=0.0)) == fa.FA_ERR_INVALID_ARG
+    assert call(base_problem(dtype=fa.FA_FP8_E4M3)) == fa.FA_ERR_UNSUPPORTED
+    p = base_problem()
+    assert fa.lib.fa_bwd_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None) == fa.FA_ERR_INVALID_ARG
+    assert call(base_problem(batch=0)) == 0

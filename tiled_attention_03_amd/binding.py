@@ -21,8 +21,8 @@ FA_BNSD, FA_BSH = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_EXPLICIT, FA_MASK_MODALITY, FA_MASK_PADDING = 0, 1, 2, 4, 8
 FA_PSE_NONE, FA_PSE_ALIBI, FA_PSE_DENSE = 0, 1, 2
 
-ENTRY_POINTS = ("fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_prep", "fa_bwd_main",
-                "fa_bwd_post", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8", "fa_maxsim",
+ENTRY_POINTS = ("fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_prep",
+                "fa_bwd_main", "fa_bwd_post", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8", "fa_maxsim",
                 "fa_status_str", "fa_abi_version")
 
 _DTYPES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
@@ -99,6 +99,7 @@ def _load():
         "fa_fwd": [P, vp, vp, vp, vp, vp, vp],
         "fa_bwd_workspace_size": [P, ctypes.POINTER(sz)],
         "fa_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "fa_bwd_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "fa_bwd_prep": [P, vp, vp, vp, sz, vp],
         "fa_bwd_main": [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "fa_bwd_post": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -375,6 +376,24 @@ def bwd(q, k, v, o, lse, do, *, heads: int, layout: str = "BNSD", workspace=None
     _check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream()), "fa_bwd")
     return (dq, dk, dv) if dpse is None else (dq, dk, dv, dpse)
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, *, heads: int, layout: str = "BNSD", **kw):
+    """fa_bwd_noalloc: the backward into the caller's dq, dk, dv without a
+    workspace (the library's static device scratch holds the row terms); the
+    binding allocates nothing either."""
+    _contig(q, k, v, o, lse, do, dq, dk, dv)
+    _same(v, k, q.dtype, q.device, "v")
+    _same(o, q, q.dtype, q.device, "o")
+    _same(do, q, q.dtype, q.device, "do")
+    p, keep = make_problem(q, k, heads=heads, layout=layout, **kw)
+    _lse_ok(lse, p, q.device)
+    gdt = torch.float32 if p.grad_f32 and q.dtype != torch.float32 else q.dtype
+    for t, like, what in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _same(t, like, gdt, q.device, what)
+    _check(lib.fa_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _stream()), "fa_bwd_noalloc")
+    return dq, dk, dv
 
 
 class Plan:

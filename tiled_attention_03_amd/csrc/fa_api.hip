@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa_launch.h"
 
 using namespace fa;
@@ -151,6 +153,33 @@ fa_status workspace_ok(const fa_problem *p, const void *ws, size_t bytes) {
 
 void bind_workspace(Params &r, void *ws) { r.delta = (float *)ws; }
 
+// ---- device scratch of the allocation-free backward (fa_bwd_noalloc): the
+// row terms D_i live in this array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes the array's name to a kernel or a copy (on the host it is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The scratch array's device address on the current device.
+fa_status current_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::call_once(scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return FA_ERR_HIP;
+  *out = scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,6 +296,23 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
   if ((st = fa_bwd_main(p, q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, stream)) != FA_OK)
     return st;
   return fa_bwd_post(p, q, k, v, lse, dout, dq, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_noalloc(const fa_problem *p, const void *q, const void *k, const void *v,
+                         const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                         void *dv, hipStream_t stream) {
+  fa_status st = check_problem(p);
+  if (st != FA_OK) return st;
+  if (p->dtype == FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if (keys_without_queries(p)) return zero_kv_grads(p, dk, dv, stream);
+  if (empty_problem(p)) return FA_OK;
+  if (!tensor_ok(q) || !ktensor_ok(p, k) || !ktensor_ok(p, v) || !tensor_ok(o) || !lse ||
+      !tensor_ok(dout) || !tensor_ok(dq) || !ktensor_ok(p, dk) || !ktensor_ok(p, dv))
+    return FA_ERR_INVALID_ARG;
+  if (delta_bytes(p) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if ((st = current_scratch(&ws)) != FA_OK) return st;
+  return fa_bwd(p, q, k, v, o, lse, dout, dq, dk, dv, ws, FA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 fa_status fa_fwd_fp8_workspace_size(const fa_problem *p, size_t *bytes) {
