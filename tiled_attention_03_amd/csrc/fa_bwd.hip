@@ -229,6 +229,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
 #pragma unroll
           for (int q = 0; q < 4; ++q) kq[q] >>= (l & 3);
         }
+        // padding, modality and explicit rules of the block's 32 queries for key my_j
+        uint32_t qm = 0u;
+        {
+          bool key_ok = my_j < p.Sk;
+          if (key_ok && (flags & FA_MASK_PADDING)) key_ok = p.key_valid[(int64_t)b * p.Sk + my_j] != 0;
+          uint32_t col_allow = 0u;
+          if ((flags & FA_MASK_MODALITY) && my_j < p.Sk) {
+            const int mk = p.kmod[(int64_t)b * p.Sk + my_j];
+            for (int mm = 0; mm < p.num_modalities; ++mm)
+              col_allow |= (uint32_t)((p.allow_bits >> (8 * mm + mk)) & 1u) << mm;
+          }
+          qm = col_querymask(p, b, h, my_j, i0, key_ok, col_allow, l);
+        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const f32x4 ls = *(const f32x4 *)&lse_s[cur][8 * rr + 4 * g];
@@ -237,8 +250,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
           for (int q = 0; q < 4; ++q) {
             const int r = 4 * rr + q;
             const int i = i0 + 8 * rr + 4 * g + q;
-            bool ok = i < p.Sq && my_j < p.Sk;
-            if (ok) ok = allowed_elem(p, b, h, i, my_j);
+            const bool ok = ((qm >> (8 * rr + 4 * g + q)) & 1u) && (!causal || my_j <= i);
             float pr = 0.f;
             if (ok) {
               float t = s[r] * c_log2;

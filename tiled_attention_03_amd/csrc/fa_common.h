@@ -172,26 +172,64 @@ __device__ __forceinline__ bool modality_ok(const Params &p, int mq, int mk, int
   return ok || (p.allow_diag && i == j);
 }
 
-// Everything except the causal rule and the S_k bound, which the tile loops
-// handle arithmetically.
+// Everything except the S_k bound, which the tile loops handle
+// arithmetically.  No early exit: the loads of the different rules do not
+// depend on each other, so the loads of a whole unrolled block of elements
+// can be in flight together.
 __device__ __forceinline__ bool allowed_elem(const Params &p, int b, int h, int i, int j) {
   const uint32_t f = p.mask_flags;
-  if (f & FA_MASK_CAUSAL) {
-    if (j > i) return false;
-  }
-  if (f & FA_MASK_PADDING) {
-    if (!p.key_valid[(int64_t)b * p.Sk + j]) return false;
-  }
+  bool ok = !(f & FA_MASK_CAUSAL) || j <= i;
+  if (f & FA_MASK_PADDING) ok &= p.key_valid[(int64_t)b * p.Sk + j] != 0;
   if (f & FA_MASK_MODALITY) {
-    int mq = p.qmod[(int64_t)b * p.Sq + i];
-    int mk = p.kmod[(int64_t)b * p.Sk + j];
-    if (!modality_ok(p, mq, mk, i, j)) return false;
+    const int mq = p.qmod[(int64_t)b * p.Sq + i];
+    const int mk = p.kmod[(int64_t)b * p.Sk + j];
+    ok &= modality_ok(p, mq, mk, i, j);
   }
-  if (f & FA_MASK_EXPLICIT) {
-    if (!p.em[(int64_t)b * p.em_sb + (int64_t)h * p.em_sh + (int64_t)i * p.em_sq + j])
-      return false;
+  if (f & FA_MASK_EXPLICIT)
+    ok &= p.em[(int64_t)b * p.em_sb + (int64_t)h * p.em_sh + (int64_t)i * p.em_sq + j] != 0;
+  return ok;
+}
+
+// The same rules (all but the causal rule) for a block of 32 elements at
+// once, built from wave-wide votes instead of one global load per element.
+// Every lane of the wave must call it (it votes).
+//
+// col_querymask: the lane's key j against the 32 queries [i0, i0 + 32): bit c
+// set iff query i0 + c < S_q may attend key j.  key_ok: key j exists and is
+// valid (padding); col_allow: the query modalities allowed to see key j's
+// modality (bit mq set = allowed).  Only the bits of the lane's own queries
+// (c = 8q + 4g + t) carry the explicit mask.
+__device__ __forceinline__ uint32_t col_querymask(const Params &p, int b, int h, int j, int i0,
+                                                  bool key_ok, uint32_t col_allow, int l) {
+  const uint32_t f = p.mask_flags;
+  const int i = i0 + (l & 31);
+  const bool in = i < p.Sq;
+  uint32_t m = (uint32_t)__ballot(in);
+  if (f & FA_MASK_MODALITY) {
+    const int mq = in ? p.qmod[(int64_t)b * p.Sq + i] : -1;
+    uint32_t allowed = 0u;
+    for (int mm = 0; mm < p.num_modalities; ++mm) {
+      const uint32_t qm = (uint32_t)__ballot(mq == mm);
+      if ((col_allow >> mm) & 1u) allowed |= qm;
+    }
+    if (p.allow_diag && j >= i0 && j < i0 + 32) allowed |= 1u << (j - i0);
+    m &= allowed;
   }
-  return true;
+  if (!key_ok) m = 0u;
+  if ((f & FA_MASK_EXPLICIT) && m) {
+    const uint8_t *col = p.em + (int64_t)b * p.em_sb + (int64_t)h * p.em_sh + j;
+    const int g = (l >> 5) & 1;
+    uint32_t ex = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = 8 * q + 4 * g + t;
+        if (i0 + c < p.Sq && col[(int64_t)(i0 + c) * p.em_sq]) ex |= 1u << c;
+      }
+    m &= ex;
+  }
+  return m;
 }
 
 // Dense bias element (natural units, unscaled).

@@ -65,6 +65,7 @@ namespace {
 // Key tiles summarised and sorted in LDS lists: at most this many (S_k up to
 // 64 * kMaxTiles); longer key ranges run the LONG instance, without lists.
 constexpr int kMaxTiles = 1024;
+constexpr int kMaxTilesSmall = 128;   // the one-wave (S_q <= 32) instance: less LDS per workgroup
 constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
 
 template <typename T, int D, int NW, int RB_, int KBN_>
@@ -74,7 +75,10 @@ struct FwdCfg {
   static constexpr int BN = 32 * KBN;      // keys per tile
   static constexpr int RB = RB_;           // 32-row blocks per wave
   static constexpr int WR = 32 * RB;       // query rows per wave
-  static constexpr int OCC = RB == 1 ? 2 : 1;   // waves per SIMD the registers allow
+  // waves per SIMD the registers allow: the one-wave instance at D = 64 (32-key
+  // tiles, small lists) fits three workgroups' waves in a SIMD's registers
+  static constexpr int OCC = RB == 1 ? (NW == 1 && D == 64 ? 3 : 2) : 1;
+  static constexpr int LT = NW == 1 ? kMaxTilesSmall : kMaxTiles;   // tiles the LDS lists hold
   static constexpr int BM = WR * NW;       // query rows per workgroup
   static constexpr int KS = D / 16;        // k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -102,12 +106,12 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   __shared__ int kv_range[2];
   __shared__ uint32_t wg_any, wg_all;   // modalities some / every row of the workgroup may attend
   __shared__ int n_list[2];             // generic tiles, all visited tiles
-  __shared__ uint32_t tsum[kMaxTiles];  // per key tile: bits 0-7 modality set of valid keys,
+  __shared__ uint32_t tsum[C::LT];  // per key tile: bits 0-7 modality set of valid keys,
                                         // bit 8 some key invalid or past S_k, bit 9 the
                                         // explicit mask allows some (row, key) of the
                                         // workgroup, bit 10 it hides some
-  __shared__ int16_t tlist[kMaxTiles];  // generic tiles, then fast tiles
-  __shared__ uint32_t fpair[kMaxTiles]; // fast tiles n and n+1 in one word (0 past the end)
+  __shared__ int16_t tlist[C::LT];  // generic tiles, then fast tiles
+  __shared__ uint32_t fpair[C::LT]; // fast tiles n and n+1 in one word (0 past the end)
 
   const int BH = p.B * p.H;
   const int lin = blockIdx.x;
@@ -129,10 +133,12 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   const T *Kg = (const T *)p.k + b * p.k_sb + h * p.k_sh;
   const T *Vg = (const T *)p.v + b * p.k_sb + h * p.k_sh;
 
-  // ---- key range of this workgroup
+  // ---- key range of this workgroup: the causal rule here; under a padding
+  // mask the tiles holding the first and last valid key narrow it further
+  // (below, from the tile summaries; the LONG instance scans the keys)
   int k_lo = 0, k_hi = p.Sk;
   if (causal) k_hi = min(k_hi, q0 + C::BM);
-  if (flags & FA_MASK_PADDING) {
+  if ((flags & FA_MASK_PADDING) && LONG) {
     if (tid == 0) { kv_range[0] = p.Sk; kv_range[1] = 0; }
     __syncthreads();
     int lo = p.Sk, hi = 0;
@@ -146,8 +152,8 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     k_lo = max(k_lo, kv_range[0]);
     k_hi = min(k_hi, kv_range[1]);
   }
-  const int kt_begin = k_lo / BN;
-  const int kt_end = k_hi > k_lo ? (k_hi + BN - 1) / BN : kt_begin;
+  int kt_begin = k_lo / BN;
+  int kt_end = k_hi > k_lo ? (k_hi + BN - 1) / BN : kt_begin;
 
   constexpr int ES = (int)sizeof(T);
   const auto Qr = make_rsrc(Qg, span_bytes(p.Sq, p.q_ss, D, ES));
@@ -183,29 +189,78 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // ---- per key tile summaries (padding / modality: one wave-wide vote per
   // tile; explicit mask: a scan of the workgroup's mask rows); modalities the
   // rows of this wave (and of the workgroup) may attend
-  const int n_kt_all = (p.Sk + BN - 1) / BN;
   const bool use_summary = (f_pad || f_mod) && !LONG;
   uint32_t allow_any = 0, allow_all = 0xffu;
-  if (tid == 0) { wg_any = 0u; wg_all = 0xffu; }
+  if (tid == 0) { wg_any = 0u; wg_all = 0xffu; kv_range[0] = kt_end; kv_range[1] = kt_begin - 1; }
+  int t_first = kt_end, t_last = kt_begin - 1;   // this wave's tiles holding a valid key
   if (use_summary) {
-    for (int kt = w; kt < n_kt_all; kt += NW) {
-      const int j = kt * BN + l;
-      const bool in_tile = l < BN;   // a tile may be narrower than the wave
-      bool valid = in_tile && j < p.Sk;
-      int m = 0;
-      if (valid && f_pad) valid = p.key_valid[(int64_t)b * p.Sk + j] != 0;
-      if (valid && f_mod) m = p.kmod[(int64_t)b * p.Sk + j];
-      uint32_t bits = __ballot(in_tile && !valid) ? 0x100u : 0u;
-      if (f_mod) {
-        for (int mm = 0; mm < p.num_modalities; ++mm)
-          if (__ballot(valid && m == mm)) bits |= 1u << mm;
-      } else if (__ballot(valid)) {
-        bits |= 1u;
+    // wave w votes on tiles w, w + NW, ...; the key loads of eight tiles are
+    // issued before any vote, so the pass costs one load round trip per eight
+    // of this wave's tiles
+    constexpr int U = 8;
+    for (int kt0 = kt_begin + w; kt0 < kt_end; kt0 += U * NW) {
+      bool valid[U];
+      int mk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = (kt0 + u * NW) * BN + l;
+        valid[u] = l < BN && kt0 + u * NW < kt_end && j < p.Sk;
+        mk[u] = 0;
+        if (valid[u] && f_pad) valid[u] = p.key_valid[(int64_t)b * p.Sk + j] != 0;
+        if (valid[u] && f_mod) mk[u] = p.kmod[(int64_t)b * p.Sk + j];
       }
-      if (l == 0) tsum[kt] = bits;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kt = kt0 + u * NW;
+        if (kt >= kt_end) break;
+        const bool in_tile = l < BN;   // a tile may be narrower than the wave
+        uint32_t bits = __ballot(in_tile && !valid[u]) ? 0x100u : 0u;
+        if (f_mod) {
+          for (int mm = 0; mm < p.num_modalities; ++mm)
+            if (__ballot(valid[u] && mk[u] == mm)) bits |= 1u << mm;
+        } else if (__ballot(valid[u])) {
+          bits |= 1u;
+        }
+        if (__ballot(valid[u])) {
+          t_first = min(t_first, kt);
+          t_last = max(t_last, kt);
+        }
+        if (l == 0) tsum[kt] = bits;
+      }
     }
   }
-  if (f_exp && !LONG) {
+  if (use_summary && f_mod) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = my_i[rb];
+      const int mq = i < p.Sq ? p.qmod[(int64_t)b * p.Sq + i] : -1;
+      for (int mm = 0; mm < p.num_modalities; ++mm) {
+        if (__ballot(mq == mm)) {
+          const uint32_t row = (uint32_t)(p.allow_bits >> (8 * mm)) & 0xffu;
+          allow_any |= row;
+          allow_all &= row;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (l == 0 && use_summary) {
+    if (f_mod) {
+      atomicOr(&wg_any, allow_any);
+      atomicAnd(&wg_all, allow_all);
+    }
+    if (f_pad) {
+      atomicMin(&kv_range[0], t_first);
+      atomicMax(&kv_range[1], t_last);
+    }
+  }
+  __syncthreads();
+  if (use_summary && f_pad) {   // tiles past the last valid key, or before the first, are out
+    const int t0 = __builtin_amdgcn_readfirstlane(kv_range[0]);
+    const int t1 = __builtin_amdgcn_readfirstlane(kv_range[1]);
+    kt_end = t1 >= t0 ? t1 + 1 : kt_begin;
+    kt_begin = t1 >= t0 ? t0 : kt_begin;
+  }
+  if (f_exp && !LONG && kt_end > kt_begin) {
     // explicit mask over the workgroup's rows [q0, q_end) and each tile's keys
     // (< S_k): bit 9 if some pair is allowed, bit 10 if some pair is hidden.
     // 16-byte reads when the rows allow them (aligned, and the workgroup's
@@ -250,26 +305,8 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
       const uint32_t eb = (__ballot(any) ? 0x200u : 0u) | (__ballot(hid) ? 0x400u : 0u);
       if (l == 0 && eb) atomicOr(&tsum[kt], eb);
     }
+    __syncthreads();
   }
-  if (use_summary && f_mod) {
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = my_i[rb];
-      const int mq = i < p.Sq ? p.qmod[(int64_t)b * p.Sq + i] : -1;
-      for (int mm = 0; mm < p.num_modalities; ++mm) {
-        if (__ballot(mq == mm)) {
-          const uint32_t row = (uint32_t)(p.allow_bits >> (8 * mm)) & 0xffu;
-          allow_any |= row;
-          allow_all &= row;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (l == 0 && use_summary && f_mod) {
-    atomicOr(&wg_any, allow_any);
-    atomicAnd(&wg_all, allow_all);
-  }
-  __syncthreads();
 
   // ---- tile lists.  Workgroup-level class of tile kt: 0 not visited,
   // 1 generic, 2 fast (no per-element work for any wave of the workgroup, or
@@ -576,7 +613,8 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // below the row, so the +1 form holds for them.  fold_max folds the tile
   // starting at key k0 into s (coefficient 0 without ALiBi: no branch, the
   // scores stay in place) and leaves lane_off and the row max (combined over
-  // the lane pair) in mx; `part` selects a quarter of the elements (0..3) or
+  // the lane pair) in mx; `part` selects one of NC equal shares of the
+  // elements (0..NC-1, one per 16-key chunk of the P V products) or
   // all of them (-1), so the work can be spread over MFMA sections.  MASK
   // applies the causal rule per element (raw score -inf where key > row, which
   // needs c_log2 > 0); on a tile wholly below the diagonal it changes nothing.
@@ -592,7 +630,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     const int adir = (causal || k0 + BN - 1 <= q0) ? 1 : -1;
     const float a = fold_pe ? adir * sl2c : 0.f;
     constexpr int NE = 16 * KBN;
-    const int e0 = part < 0 ? 0 : part * NE / 4, e1 = part < 0 ? NE : (part + 1) * NE / 4;
+    const int e0 = part < 0 ? 0 : part * NE / NC, e1 = part < 0 ? NE : (part + 1) * NE / NC;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (part <= 0) {
@@ -612,7 +650,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         sc[rb][kb][r] = (MASK && c > lim) ? -INFINITY : v;
         mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
       }
-      if (part < 0 || part == 3)
+      if (part < 0 || part == NC - 1)
         mx[rb] = max_lane_pair(fmaf(mx[rb] + (32.f * (KBN - 1)) * ash, c_log2, lane_off[rb]));
     }
   };
@@ -728,7 +766,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb][db] = Mfma<T>::mac(va[c][db], pk[rb][c], acc[rb][db]);
-      fold_max(sn, kt1 * BN, c * 4 / NC, lon, mxn, mask);
+      fold_max(sn, kt1 * BN, c, lon, mxn, mask);
       __builtin_amdgcn_sched_barrier(0x0004);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -795,13 +833,18 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
 constexpr int kRB = 1, kKBN = 2;   // tile shape: 32-row blocks per wave, 32-key blocks per tile
 constexpr int kNW = 4;             // waves per workgroup
 
-// One (dtype, head_dim): a key range of more than kMaxTiles tiles takes the
-// LONG instance; S_q <= 32 a one-wave workgroup.
+// One (dtype, head_dim): S_q <= 32 takes a one-wave workgroup (lists of
+// kMaxTilesSmall tiles); otherwise a key range of more than kMaxTiles tiles
+// takes the LONG instance.
 template <typename T, int D>
 hipError_t launch_d(const Params &p, hipStream_t s) {
   const int64_t n_kt = ((int64_t)p.Sk + 32 * kKBN - 1) / (32 * kKBN);
+  // S_q <= 32: one-wave workgroups streaming 32-key tiles (D = 64) or 64-key
+  // tiles (D = 128), so that more workgroups fit a CU's LDS
+  constexpr int KBN_S = D == 64 ? 1 : kKBN;
+  const int64_t n_kt_s = ((int64_t)p.Sk + 32 * KBN_S - 1) / (32 * KBN_S);
+  if (p.Sq <= 32 * kRB && n_kt_s <= kMaxTilesSmall) return launch_t<T, D, 1, kRB, KBN_S, false>(p, s);
   if (n_kt > kMaxTiles) return launch_t<T, D, kNW, kRB, kKBN, true>(p, s);
-  if (p.Sq <= 32 * kRB) return launch_t<T, D, 1, kRB, kKBN, false>(p, s);
   return launch_t<T, D, kNW, kRB, kKBN, false>(p, s);
 }
 
