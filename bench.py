@@ -27,7 +27,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X and % of bf16 MFMA peak"
 _CSRC = "tiled_attention_03_amd/csrc/"
 KERNEL_SOURCES = {   # files whose text decides each timed kernel's code
-    "fwd": [_CSRC + f for f in ("fa_fwd.hip", "fa_tile.h", "fa_common.h")],
+    "fwd": [_CSRC + f for f in ("fa_fwd_kernel.h", "fa_fwd_bf16_d128.hip", "fa_tile.h",
+                                "fa_common.h")],
     "bwd_main": [_CSRC + f for f in ("fa_bwd.hip", "fa_bwd_split.hip", "fa_tile.h", "fa_common.h")],
     "bwd_post": [_CSRC + f for f in ("fa_bwd.hip", "fa_tile.h", "fa_common.h")],
     "maxsim": [_CSRC + f for f in ("fa_maxsim.hip", "fa_tile.h", "fa_common.h")],
@@ -92,34 +93,43 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(pr, heads=1):
-    """The fp64 oracle timed on this host on a bounded sample of the workload:
-    forward + backward of the first ``heads`` heads at the full sequence."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - reporting only
-        threads = os.cpu_count() or 1
-    sub_q = pr.q[:, :heads].contiguous()
-    sub_k = pr.k[:, :heads].contiguous()
-    sub_v = pr.v[:, :heads].contiguous()
-    sub_do = pr.do[:, :heads].contiguous()
-    slopes = pr.alibi_slopes[:heads].clone()
+def cpu_baseline(pr, heads=0):
+    """The plain C++ fp64 oracle timed on this host on a bounded sample of the
+    workload: forward + backward of the first ``heads`` heads (default: one per
+    host thread, OpenMP over heads) at the full sequence length; plus the tiny
+    workload whole and one head of the causal workload on a single thread."""
+    from oracle import cpp
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    n = min(pr.heads, heads or threads)
+    sub = [t[:, :n].contiguous() for t in (pr.q, pr.k, pr.v, pr.do)]
+    slopes = pr.alibi_slopes[:n].clone() if pr.alibi_slopes is not None else None
+    kw = dict(causal=pr.causal, alibi_slopes=slopes, keep_prob=pr.keep_prob,
+              dropout_seed=pr.dropout_seed)
+    used = cpp.set_threads(min(threads, n))
     t0 = time.perf_counter()
-    drop = dict(keep_prob=pr.keep_prob, dropout_seed=pr.dropout_seed)
-    oracle.attention_fwd(sub_q, sub_k, sub_v, pr.scale, causal=pr.causal, alibi_slopes=slopes,
-                         **drop)
-    oracle.attention_bwd(sub_q, sub_k, sub_v, sub_do, pr.scale, causal=pr.causal,
-                         alibi_slopes=slopes, **drop)
+    cpp.attention_fwd(sub[0], sub[1], sub[2], pr.scale, **kw)
+    cpp.attention_bwd(*sub, pr.scale, **kw)
     dt = time.perf_counter() - t0
-    pairs = heads * pr.seq_q * (pr.seq_q + 1) // 2
+    pairs = n * pr.seq_q * (pr.seq_q + 1) // 2 if pr.causal else n * pr.seq_q * pr.seq_k
     flops = 14 * pr.head_dim * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    # single-threaded: the tiny workload whole, one head of the causal workload
+    from tiled_attention_03_amd import inputs
+    cpp.set_threads(1)
+    single = {}
+    for cid, nh in ((1, None), (2, 1)):
+        c = inputs.config(cid)
+        ts = [t if nh is None else t[:, :nh].contiguous() for t in (c.q, c.k, c.v, c.do)]
+        s0 = time.perf_counter()
+        cpp.attention_fwd(ts[0], ts[1], ts[2], c.scale, causal=c.causal)
+        cpp.attention_bwd(*ts, c.scale, causal=c.causal)
+        single[c.name + ("" if nh is None else f"_head0")] = round(time.perf_counter() - s0, 4)
+    cpp.set_threads(used)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(threads, n)),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"fwd+bwd of {heads} of {pr.heads} heads (b=0, h<{heads}) at S={pr.seq_q}, "
-                      f"numpy float64, algorithmic flops 14*D per visible pair"}
+            "sample": f"fwd+bwd of {n} of {pr.heads} heads (b=0, h<{n}) at S={pr.seq_q}: the plain "
+                      f"C++ fp64 oracle, one head per OpenMP thread; algorithmic flops 14*D per "
+                      f"visible pair",
+            "single_thread_seconds": single}
 
 
 def maxsim_bytes(case) -> int:
@@ -372,7 +382,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads in the CPU-baseline sample (0: one per host thread)")
     ap.add_argument("--more", default="2,3,4",
                     help="comma-separated workload ids whose forward is also timed and reported "
                          "under 'workloads' (empty: none)")

@@ -567,3 +567,41 @@ def test_key_range_past_one_tile_list(B, H, Sq, Sk, D, dtype, layout, mask, seed
         pr.explicit_mask = block_mask(B, Sq, Sk, seed, 64, 4096)
     o, lse = check_fwd(pr)
     check_bwd(pr, o, lse)
+
+
+# ----------------------------------------------------------------------------------
+# run-time switches: FA_TILE picks the forward workgroup shape (results agree with
+# the oracle either way), FA_LOG reports the kernel each call launches
+
+@pytest.mark.parametrize("tile,Sq,want", [("wg4", 32, "NW=4"), ("wg1", 200, "NW=1"),
+                                          ("auto", 32, "NW=1"), ("auto", 200, "NW=4")])
+def test_tile_switch_and_launch_log(monkeypatch, capfd, tile, Sq, want):
+    pr = make_case(2, 3, Sq, 300, 64, torch.bfloat16, "BSH", "padding", 3300 + Sq)
+    monkeypatch.setenv("FA_TILE", tile)
+    monkeypatch.setenv("FA_LOG", "1")
+    capfd.readouterr()
+    o, lse = check_fwd(pr)
+    err = capfd.readouterr().err
+    line = [ln for ln in err.splitlines() if ln.startswith("[libfa] fa_fwd")]
+    assert line and want in line[-1] and "masks=padding" in line[-1], err
+    check_bwd(pr, o, lse)
+    err = capfd.readouterr().err
+    assert "[libfa] fa_bwd_main" in err and "[libfa] fa_bwd_post" in err
+
+
+# ----------------------------------------------------------------------------------
+# the workloads against the plain C++ fp64 oracle as well (the tests above read the
+# numpy one; the two agree to 1e-11 on the CPU pins)
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_workloads_against_cpp_oracle(cid):
+    from oracle import cpp
+    pr = inputs.config(cid)
+    print(f"\n{pr.name} (C++ oracle)")
+    o, lse = gpu_fwd(pr)
+    O, L = cpp.problem_fwd(pr)
+    assert_close("O", o, O, pr.dtype)
+    assert_lse(lse, L)
+    g = gpu_bwd(pr, o, lse)
+    for name, a, r in zip(("dQ", "dK", "dV"), g, cpp.problem_bwd(pr)):
+        assert_close(name, a, r, pr.dtype)

@@ -2,6 +2,8 @@
 // The contract of every entry point is documented in include/fa.h.
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -9,6 +11,43 @@
 #include "fa_launch.h"
 
 using namespace fa;
+
+namespace fa {
+
+// The switches are read at every call (getenv is cheap next to a launch), so
+// a process may change them between calls.
+bool log_enabled() {
+  const char *lg = getenv("FA_LOG");
+  return lg && *lg && strcmp(lg, "0") != 0;
+}
+
+int tile_override() {
+  const char *tl = getenv("FA_TILE");
+  if (tl && strcmp(tl, "wg4") == 0) return kTileWg4;
+  if (tl && strcmp(tl, "wg1") == 0) return kTileWg1;
+  return kTileAuto;
+}
+
+void log_launch(const char *what, const char *instance, long long grid, int block,
+                const Params &p) {
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lk(mu);
+  const char *masks[4] = {"causal", "explicit", "modality", "padding"};
+  char mk[64] = "";
+  for (int i = 0; i < 4; ++i)
+    if (p.mask_flags & (1u << i)) {
+      if (mk[0]) strcat(mk, "+");
+      strcat(mk, masks[i]);
+    }
+  fprintf(stderr,
+          "[libfa] %s: B=%d H=%d S_q=%d S_k=%d D=%d masks=%s pse=%s dropout=%d -> %s grid=%lld "
+          "block=%d\n",
+          what, p.B, p.H, p.Sq, p.Sk, p.D, mk[0] ? mk : "none",
+          p.pse_kind == FA_PSE_ALIBI ? "alibi" : p.pse_kind == FA_PSE_DENSE ? "dense" : "none",
+          p.dropout, instance, grid, block);
+}
+
+}  // namespace fa
 
 namespace {
 

@@ -34,6 +34,8 @@
 #include <algorithm>
 #include <climits>
 
+#include <stdio.h>
+
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -828,6 +830,12 @@ hipError_t launch_kv(const Params &p, hipStream_t s) {
   if (blocks == 0) return hipGetLastError();
   const bool extra = p.grad_f32 || p.dpse;
   const dim3 grid((unsigned)blocks), block(NWB * 64);
+  if (log_enabled()) {
+    char name[96];
+    snprintf(name, sizeof(name), "bwd_kv_kernel<D=%d%s%s> (one-role key pass)", D,
+             p.dropout ? ", DROP" : "", extra ? ", EXTRA" : "");
+    log_launch("fa_bwd_main", name, (long long)blocks, NWB * 64, p);
+  }
   if (p.dropout) {
     if (extra) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true>), grid, block, 0, s, p, n_ktiles);
     else hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false>), grid, block, 0, s, p, n_ktiles);
@@ -845,6 +853,12 @@ hipError_t launch_q(const Params &p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const bool extra = p.grad_f32 != 0;
   const dim3 grid((unsigned)blocks), block(NWB * 64);
+  if (log_enabled()) {
+    char name[96];
+    snprintf(name, sizeof(name), "bwd_q_kernel<D=%d%s%s> (query pass)", D,
+             p.dropout ? ", DROP" : "", extra ? ", EXTRA" : "");
+    log_launch("fa_bwd_post", name, (long long)blocks, NWB * 64, p);
+  }
   if (p.dropout) {
     if (extra) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true>), grid, block, 0, s, p, n_qtiles);
     else hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false>), grid, block, 0, s, p, n_qtiles);

@@ -32,6 +32,8 @@
 // sees key 0, so no row has an empty softmax here and the LSE is finite.
 #include <climits>
 
+#include <stdio.h>
+
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -484,6 +486,12 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
   const int n_ktiles = (p.Sk + SKB - 1) / SKB;
   const int64_t blocks = (int64_t)n_ktiles * p.B * p.H;
   if (blocks == 0) return hipSuccess;
+  if (log_enabled()) {
+    char name[96];
+    snprintf(name, sizeof(name), "bwd_kv_split_kernel<D=%d%s> (producer/consumer key pass)", D,
+             p.dropout ? ", DROP" : "");
+    log_launch("fa_bwd_main", name, (long long)blocks, 2 * NPW * 64, p);
+  }
   if (p.dropout)
     hipLaunchKernelGGL((bwd_kv_split_kernel<T, D, true>), dim3((unsigned)blocks),
                        dim3(2 * NPW * 64), 0, s, p, n_ktiles);

@@ -56,6 +56,8 @@
 // rescale rarely fires.
 #pragma once
 
+#include <stdio.h>
+
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -820,6 +822,13 @@ hipError_t launch_t(const Params &p, hipStream_t s) {
   const bool fold = p.pse_kind == FA_PSE_ALIBI && !(p.mask_flags & FA_MASK_CAUSAL);
   const dim3 grid((unsigned)blocks), block(C::NT);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, p, n_qtiles); };
+  if (log_enabled()) {
+    char name[128];
+    snprintf(name, sizeof(name), "fwd_mfma_kernel<%s, D=%d, NW=%d, RB=%d, KBN=%d%s%s%s>",
+             std::is_same<T, __bf16>::value ? "bf16" : "f16", D, NW, RB, KBN,
+             p.dropout ? ", DROP" : "", fold ? ", FOLD" : "", LONG ? ", LONG" : "");
+    log_launch("fa_fwd", name, (long long)blocks, C::NT, p);
+  }
   if (p.dropout) {
     if (fold) go(fwd_mfma_kernel<T, D, NW, RB, KBN, true, true, LONG>);
     else go(fwd_mfma_kernel<T, D, NW, RB, KBN, true, false, LONG>);
@@ -843,7 +852,10 @@ hipError_t launch_d(const Params &p, hipStream_t s) {
   // tiles (D = 128), so that more workgroups fit a CU's LDS
   constexpr int KBN_S = D == 64 ? 1 : kKBN;
   const int64_t n_kt_s = ((int64_t)p.Sk + 32 * KBN_S - 1) / (32 * KBN_S);
-  if (p.Sq <= 32 * kRB && n_kt_s <= kMaxTilesSmall) return launch_t<T, D, 1, kRB, KBN_S, false>(p, s);
+  const int ov = tile_override();
+  const bool small = ov == kTileWg1 ? n_kt_s <= kMaxTilesSmall
+                                    : ov != kTileWg4 && p.Sq <= 32 * kRB && n_kt_s <= kMaxTilesSmall;
+  if (small) return launch_t<T, D, 1, kRB, KBN_S, false>(p, s);
   if (n_kt > kMaxTiles) return launch_t<T, D, kNW, kRB, kKBN, true>(p, s);
   return launch_t<T, D, kNW, kRB, kKBN, false>(p, s);
 }

@@ -9,6 +9,21 @@
 
 namespace fa {
 
+// Run-time switches read from the environment at each call (host side only):
+//   FA_LOG=1   every call prints the kernel instance it launches and its grid
+//              on stderr (one line per launch);
+//   FA_TILE=   forward workgroup shape, for sweeps: "auto" (default: one-wave
+//              workgroups for S_q <= 32, four-wave ones otherwise), "wg4"
+//              (four-wave workgroups for every S_q), "wg1" (one-wave
+//              workgroups for every S_q whose key range fits their lists).
+// Unknown FA_TILE values count as "auto".  The choice never changes results
+// beyond rounding order.
+enum { kTileAuto = 0, kTileWg4 = 1, kTileWg1 = 2 };
+bool log_enabled();
+int tile_override();
+void log_launch(const char *what, const char *instance, long long grid, int block,
+                const Params &p);
+
 // Forward, bf16/f16 MFMA path (D = 64 or 128), and its per-(dtype, D) instances.
 hipError_t launch_fwd_mfma(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_fwd_bf16_d64(const Params &p, hipStream_t s);
