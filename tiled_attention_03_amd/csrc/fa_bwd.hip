@@ -176,10 +176,33 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
     // per-element work) or general.  Blocks the mask hides wholly take the
     // general path, which yields P = dS = 0; keeping the accumulation
     // unconditional lets the dK/dV accumulators stay in place.
-    bool general = f_elem || dense || DROP || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
+    bool general = dense || DROP || (jw + 32 > p.Sk) || (i0 + QB > p.Sq);
     if (causal && jw + 31 > i0) general = true;
     if (alibi && !(i0 >= jw + 31)) general = true;   // fast ALiBi form needs i >= j
-    {
+    // padding, modality and explicit rules of the block's 32 queries for the
+    // lane's key (bit c: query i0 + c may attend key my_j), from wave votes.  A
+    // block they hide from every key of the wave is skipped (it adds nothing);
+    // one they show wholly to every key needs no per-element work.
+    uint32_t qm;
+    bool skip = false;
+    if (!f_elem) {   // the bounds alone
+      const uint32_t rows = (uint32_t)__ballot(i0 + (l & 31) < p.Sq);
+      qm = my_j < p.Sk ? rows : 0u;
+    } else {
+      bool key_ok = my_j < p.Sk;
+      if (key_ok && (flags & FA_MASK_PADDING)) key_ok = p.key_valid[(int64_t)b * p.Sk + my_j] != 0;
+      uint32_t col_allow = 0u;
+      if ((flags & FA_MASK_MODALITY) && my_j < p.Sk) {
+        const int mk = p.kmod[(int64_t)b * p.Sk + my_j];
+        for (int mm = 0; mm < p.num_modalities; ++mm)
+          col_allow |= (uint32_t)((p.allow_bits >> (8 * mm + mk)) & 1u) << mm;
+      }
+      qm = col_querymask(p, b, h, my_j, i0, key_ok, col_allow, l);
+      const uint32_t own = 0x0F0F0F0Fu << (4 * g);   // this lane's queries' bits
+      skip = __ballot((qm & own) != 0) == 0;
+      if (__ballot((qm & own) != own) != 0) general = true;
+    }
+    if (!skip) {
       f32x16 s = f32x16{}, dp = f32x16{};
       // operand reads are issued in batches ahead of their MFMAs
 #pragma unroll
@@ -230,19 +253,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(Params p, int n_ktiles) 
           kq[3] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
 #pragma unroll
           for (int q = 0; q < 4; ++q) kq[q] >>= (l & 3);
-        }
-        // padding, modality and explicit rules of the block's 32 queries for key my_j
-        uint32_t qm = 0u;
-        {
-          bool key_ok = my_j < p.Sk;
-          if (key_ok && (flags & FA_MASK_PADDING)) key_ok = p.key_valid[(int64_t)b * p.Sk + my_j] != 0;
-          uint32_t col_allow = 0u;
-          if ((flags & FA_MASK_MODALITY) && my_j < p.Sk) {
-            const int mk = p.kmod[(int64_t)b * p.Sk + my_j];
-            for (int mm = 0; mm < p.num_modalities; ++mm)
-              col_allow |= (uint32_t)((p.allow_bits >> (8 * mm + mk)) & 1u) << mm;
-          }
-          qm = col_querymask(p, b, h, my_j, i0, key_ok, col_allow, l);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -617,12 +627,49 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     // (the fast ALiBi form folds slope / c_log2 into raw scores: c_log2 > kRawMinC)
     // (in the general phase dropout keeps every tile on the per-element code,
     // whose fast-tile branch draws no keep mask)
-    bool general = f_elem || dense || (GEN && DROP) || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
+    bool general = dense || (GEN && DROP) || (k0 + KBQ > p.Sk) || (qw + 32 > p.Sq) ||
                    (alibi && !(c_log2 > kRawMinC));
     if (causal && k0 + KBQ - 1 > qw) general = true;
     if (alibi && !(k0 + KBQ - 1 <= qw)) general = true;
+    // padding and modality rules over the wave's 32 rows and the tile's 64 keys,
+    // from wave votes: a tile they hide wholly is skipped, one they show wholly
+    // needs no per-element work (an explicit mask always takes the per-element
+    // code)
+    bool skip = false;
+    if (GEN && f_elem) {
+      static_assert(KBQ == 64, "one key per lane");
+      const int j = k0 + l;
+      const bool in = j < p.Sk;
+      bool kv = in;
+      if (in && (flags & FA_MASK_PADDING)) kv = p.key_valid[(int64_t)b * p.Sk + j] != 0;
+      const uint64_t kvm = __ballot(kv);
+      bool any = kvm != 0;
+      bool full = !(flags & FA_MASK_EXPLICIT) && kvm == __ballot(in);
+      if (flags & FA_MASK_MODALITY) {
+        const int mk = kv ? p.kmod[(int64_t)b * p.Sk + j] : -1;
+        const int mq = my_i < p.Sq ? p.qmod[(int64_t)b * p.Sq + my_i] : -1;
+        bool some = false, all = true;
+        for (int a = 0; a < p.num_modalities; ++a) {
+          if (!__ballot(mq == a)) continue;
+          const uint32_t row = (uint32_t)(p.allow_bits >> (8 * a)) & 0xffu;
+          for (int c = 0; c < p.num_modalities; ++c) {
+            if (!__ballot(mk == c)) continue;
+            if ((row >> c) & 1u) some = true;
+            else all = false;
+          }
+        }
+        const bool diag = p.allow_diag && k0 < qw + 32 && k0 + KBQ > qw;
+        if (!some && !diag) any = false;
+        if (!all || diag) full = false;
+      }
+      skip = !any;
+      if (!full) general = true;
+    } else if (f_elem) {
+      general = true;
+    }
     if (!GEN) general = false;   // the fast phase only visits tiles fast for every wave
-    {
+    if (qw >= p.Sq) skip = true;   // a wave past the last query row has nothing to add
+    if (!skip) {
       const float off = (alibi ? sl2 * (float)(k0 + 4 * g - my_i) : 0.f) - lse2;
       // one 32-key block at a time (LSE is known: no row max to wait for)
 #pragma unroll
