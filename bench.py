@@ -384,7 +384,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the CPU-baseline sample (0: one per host thread)")
-    ap.add_argument("--more", default="2,3,4",
+    ap.add_argument("--more", default="1,2,3,4",
                     help="comma-separated workload ids whose forward is also timed and reported "
                          "under 'workloads' (empty: none)")
     ap.add_argument("--keep-prob", type=float, default=1.0,

@@ -7,12 +7,13 @@
 // softmax" of its section 1 and of the NPU FlashAttention study's flow
 // description).
 //
-// Workgroup = NW waves, one wave per SIMD (each wave has the whole register
-// file).  A wave owns RB = 2 blocks of 32 query rows, so every K or V operand
-// read from LDS feeds two MFMAs (LDS read traffic per flop is what bounds a
-// one-operand-from-LDS design); the workgroup's BM = 32*RB*NW rows share one
-// stream of K/V tiles of BN = 64 keys.  The products are arranged so that a
-// lane owns one query row of each block for the whole kernel:
+// Workgroup = NW waves, each owning RB blocks of 32 query rows (the tile
+// table at the end of this file: RB = 1, NW = 4 with 64-key tiles, two
+// workgroups and so two waves per SIMD; S_q <= 32 takes one-wave workgroups,
+// with 32-key tiles at D = 64 and three waves per SIMD).  The workgroup's
+// BM = 32*RB*NW rows share one stream of K/V tiles of BN = 32*KBN keys.  The
+// products are arranged so that a lane owns one query row of each block for
+// the whole kernel:
 //
 //   S^T (keys x queries) = K . Q^T     v_mfma_f32_32x32x16, A = K from LDS,
 //                                      B = Q^T kept in registers
@@ -34,9 +35,11 @@
 // Two phases.  The workgroup first sorts its key tiles: "fast" tiles need no
 // per-element work for any of its rows (wholly visible under the causal rule,
 // within S_k, ALiBi on one side of the diagonal, every key valid and of a
-// modality all rows may attend); the rest are "generic" (the causal diagonal
-// band, the S_k tail, explicit masks, dense bias, ...).  Tiles no row can see
-// are dropped.
+// modality all rows may attend, an explicit mask allowing every pair); the
+// rest are "generic" (the causal diagonal band, the S_k tail, partly masked
+// tiles, dense bias, ...).  Tiles no row can see are dropped.  The summaries
+// behind this come from one pass of wave votes over the key flags (padding,
+// modality) and a scan of the workgroup's explicit-mask rows.
 //
 //   generic phase: one tile per step; each wave classifies the tile for its
 //     own rows (nothing visible: skip; no element work: fast; else per-element
