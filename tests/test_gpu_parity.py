@@ -547,6 +547,26 @@ def test_block_mask_per_head_with_empty_query_tiles():
     check_bwd(pr, o, lse)
 
 
+def test_explicit_mask_rows_with_padded_stride():
+    """An explicit mask whose rows sit at a 16-byte-multiple stride wider than S_k
+    (a view of a wider mask; the extra columns hold values that would change the
+    result if read): the same result as the contiguous mask."""
+    B, H, Sq, Sk = 2, 2, 200, 250
+    pr = make_case(B, H, Sq, Sk, 64, torch.bfloat16, "BNSD", "explicit", 3120)
+    pr.explicit_mask = block_mask(B, Sq, Sk, 3120, 64, 64)
+    wide = torch.zeros(B, 1, Sq, 256, dtype=torch.bool, device=DEV)
+    wide[..., Sk:] = True
+    wide[..., :Sk] = pr.explicit_mask.to(DEV)
+    view = wide[..., :Sk]
+    assert view.stride(2) == 256
+    kw = fa.problem_kwargs(pr, DEV)
+    kw["explicit_mask"] = view
+    q, k, v = (t.to(DEV) for t in (pr.q, pr.k, pr.v))
+    o, lse = fa.fwd(q, k, v, heads=pr.heads, layout=pr.layout, **kw)
+    torch.cuda.synchronize()
+    check_fwd(pr, o, lse)
+
+
 # ----------------------------------------------------------------------------------
 # key ranges longer than one tile list (1024 tiles of 64 keys): the forward walks
 # them in chunks
@@ -570,11 +590,50 @@ def test_key_range_past_one_tile_list(B, H, Sq, Sk, D, dtype, layout, mask, seed
 
 
 # ----------------------------------------------------------------------------------
+# short query blocks (S_q <= 32, S_k <= 2048, causal / padding masks, ALiBi or no
+# bias): one wave per (batch, head) with K streamed into registers; every tile takes
+# the per-element rules.  Past those limits the list-based one-wave workgroup runs.
+
+SHORT = [
+    (3, 4, 32, 512, 64, torch.bfloat16, "BSH", "padding", 3400),
+    (2, 3, 17, 2048, 64, torch.bfloat16, "BNSD", "padding", 3401),
+    (2, 3, 32, 2049, 64, torch.bfloat16, "BNSD", "padding", 3402),
+    (2, 2, 1, 33, 128, torch.float16, "BSH", "causal+alibi", 3403),
+    (2, 2, 32, 100, 128, torch.bfloat16, "BNSD", "alibi", 3404),
+    (2, 2, 20, 31, 64, torch.float16, "BNSD", "causal+padding", 3405),
+    (4, 2, 32, 700, 64, torch.bfloat16, "BSH", "holes", 3406),
+    (2, 3, 29, 96, 128, torch.bfloat16, "BSH", "none", 3407),
+    (1, 2, 32, 1, 64, torch.bfloat16, "BNSD", "none", 3408),
+    (2, 2, 24, 500, 64, torch.bfloat16, "BNSD", "explicit", 3409),
+]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,dtype,layout,mask,seed", SHORT,
+                         ids=[f"{c[6]}-D{c[4]}-{c[2]}x{c[3]}-{c[7]}" for c in SHORT])
+def test_short_query_blocks(B, H, Sq, Sk, D, dtype, layout, mask, seed):
+    pr = make_case(B, H, Sq, Sk, D, dtype, layout, mask, seed)
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
+def test_short_query_sample_without_valid_keys():
+    """A sample whose keys are all padding: its rows get O = 0 and LSE = -inf, the
+    other samples are unaffected."""
+    pr = make_case(3, 2, 32, 300, 64, torch.bfloat16, "BSH", "padding", 3410)
+    pr.key_valid[1] = False
+    o, lse = check_fwd(pr)
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    check_bwd(pr, o, lse)
+
+
+# ----------------------------------------------------------------------------------
 # run-time switches: FA_TILE picks the forward workgroup shape (results agree with
 # the oracle either way), FA_LOG reports the kernel each call launches
 
 @pytest.mark.parametrize("tile,Sq,want", [("wg4", 32, "NW=4"), ("wg1", 200, "NW=1"),
-                                          ("auto", 32, "NW=1"), ("auto", 200, "NW=4")])
+                                          ("wg1", 32, "NW=1"), ("auto", 32, "fwd_short_kernel"),
+                                          ("short", 20, "fwd_short_kernel"),
+                                          ("short", 200, "NW=4"), ("auto", 200, "NW=4")])
 def test_tile_switch_and_launch_log(monkeypatch, capfd, tile, Sq, want):
     pr = make_case(2, 3, Sq, 300, 64, torch.bfloat16, "BSH", "padding", 3300 + Sq)
     monkeypatch.setenv("FA_TILE", tile)

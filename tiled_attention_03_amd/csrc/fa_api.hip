@@ -25,6 +25,7 @@ int tile_override() {
   const char *tl = getenv("FA_TILE");
   if (tl && strcmp(tl, "wg4") == 0) return kTileWg4;
   if (tl && strcmp(tl, "wg1") == 0) return kTileWg1;
+  if (tl && strcmp(tl, "short") == 0) return kTileShort;
   return kTileAuto;
 }
 

@@ -61,6 +61,7 @@
 
 #include <stdio.h>
 
+#include "fa_fwd_short.h"
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -268,14 +269,14 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   if (f_exp && !LONG && kt_end > kt_begin) {
     // explicit mask over the workgroup's rows [q0, q_end) and each tile's keys
     // (< S_k): bit 9 if some pair is allowed, bit 10 if some pair is hidden.
-    // 16-byte reads when the rows allow them (aligned, and the workgroup's
-    // rows within a 32-bit buffer range from row q0; bytes past it read as
-    // zeros), else one byte per lane.
+    // 16-byte reads when the rows allow them (aligned, S_k a multiple of 16 so
+    // that no read crosses the end of the range, and the workgroup's rows
+    // within a 32-bit buffer range from row q0), else one byte per lane.
     const int q_end = min(q0 + C::BM, p.Sq);
     const uint8_t *emb = p.em + (int64_t)b * p.em_sb + (int64_t)h * p.em_sh;
     const int64_t em_sq = p.em_sq;
     const int64_t em_span = (int64_t)(q_end - 1 - q0) * em_sq + p.Sk;
-    const bool em_vec = ((uintptr_t)emb & 15u) == 0 && (em_sq & 15) == 0 &&
+    const bool em_vec = ((uintptr_t)emb & 15u) == 0 && (em_sq & 15) == 0 && (p.Sk & 15) == 0 &&
                         em_span < ((int64_t)1 << 31);
     const auto Er = make_rsrc(em_vec ? emb + (int64_t)q0 * em_sq : nullptr,
                               em_vec ? (uint32_t)em_span : 0u);
@@ -856,6 +857,7 @@ hipError_t launch_d(const Params &p, hipStream_t s) {
   constexpr int KBN_S = D == 64 ? 1 : kKBN;
   const int64_t n_kt_s = ((int64_t)p.Sk + 32 * KBN_S - 1) / (32 * KBN_S);
   const int ov = tile_override();
+  if ((ov == kTileAuto || ov == kTileShort) && short_fits(p)) return launch_short<T, D>(p, s);
   const bool small = ov == kTileWg1 ? n_kt_s <= kMaxTilesSmall
                                     : ov != kTileWg4 && p.Sq <= 32 * kRB && n_kt_s <= kMaxTilesSmall;
   if (small) return launch_t<T, D, 1, kRB, KBN_S, false>(p, s);

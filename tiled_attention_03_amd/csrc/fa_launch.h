@@ -12,13 +12,15 @@ namespace fa {
 // Run-time switches read from the environment at each call (host side only):
 //   FA_LOG=1   every call prints the kernel instance it launches and its grid
 //              on stderr (one line per launch);
-//   FA_TILE=   forward workgroup shape, for sweeps: "auto" (default: one-wave
-//              workgroups for S_q <= 32, four-wave ones otherwise), "wg4"
-//              (four-wave workgroups for every S_q), "wg1" (one-wave
-//              workgroups for every S_q whose key range fits their lists).
+//   FA_TILE=   forward workgroup shape, for sweeps: "auto" (default: the
+//              short-query kernel where it applies, else one-wave workgroups
+//              for S_q <= 32 and four-wave ones otherwise), "short" (the same
+//              as auto), "wg4" (four-wave workgroups for every S_q), "wg1"
+//              (one-wave list-based workgroups for every S_q whose key range
+//              fits their lists).
 // Unknown FA_TILE values count as "auto".  The choice never changes results
 // beyond rounding order.
-enum { kTileAuto = 0, kTileWg4 = 1, kTileWg1 = 2 };
+enum { kTileAuto = 0, kTileWg4 = 1, kTileWg1 = 2, kTileShort = 3 };
 bool log_enabled();
 int tile_override();
 void log_launch(const char *what, const char *instance, long long grid, int block,
