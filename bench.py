@@ -94,13 +94,13 @@ def traffic_for(kernel: str):
 
 
 def cpu_baseline(pr, heads=0):
-    """The plain C++ fp64 oracle timed on this host on a bounded sample of the
-    workload: forward + backward of the first ``heads`` heads (default: one per
-    host thread, OpenMP over heads) at the full sequence length; plus the tiny
-    workload whole and one head of the causal workload on a single thread."""
+    """The plain C++ fp64 oracle timed on this host: forward + backward of the
+    first ``heads`` heads (default: all of them, the whole workload), OpenMP
+    over heads; plus the tiny and the causal workloads whole on a single
+    thread."""
     from oracle import cpp
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    n = min(pr.heads, heads or threads)
+    n = min(pr.heads, heads or pr.heads)
     sub = [t[:, :n].contiguous() for t in (pr.q, pr.k, pr.v, pr.do)]
     slopes = pr.alibi_slopes[:n].clone() if pr.alibi_slopes is not None else None
     kw = dict(causal=pr.causal, alibi_slopes=slopes, keep_prob=pr.keep_prob,
@@ -112,23 +112,23 @@ def cpu_baseline(pr, heads=0):
     dt = time.perf_counter() - t0
     pairs = n * pr.seq_q * (pr.seq_q + 1) // 2 if pr.causal else n * pr.seq_q * pr.seq_k
     flops = 14 * pr.head_dim * pairs
-    # single-threaded: the tiny workload whole, one head of the causal workload
+    # single-threaded: the tiny and the causal workloads whole
     from tiled_attention_03_amd import inputs
     cpp.set_threads(1)
     single = {}
-    for cid, nh in ((1, None), (2, 1)):
+    for cid in (1, 2):
         c = inputs.config(cid)
-        ts = [t if nh is None else t[:, :nh].contiguous() for t in (c.q, c.k, c.v, c.do)]
         s0 = time.perf_counter()
-        cpp.attention_fwd(ts[0], ts[1], ts[2], c.scale, causal=c.causal)
-        cpp.attention_bwd(*ts, c.scale, causal=c.causal)
-        single[c.name + ("" if nh is None else f"_head0")] = round(time.perf_counter() - s0, 4)
+        cpp.attention_fwd(c.q, c.k, c.v, c.scale, causal=c.causal)
+        cpp.attention_bwd(c.q, c.k, c.v, c.do, c.scale, causal=c.causal)
+        single[c.name] = round(time.perf_counter() - s0, 4)
     cpp.set_threads(used)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(threads, n)),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"fwd+bwd of {n} of {pr.heads} heads (b=0, h<{n}) at S={pr.seq_q}: the plain "
-                      f"C++ fp64 oracle, one head per OpenMP thread; algorithmic flops 14*D per "
-                      f"visible pair",
+            "sample": (f"fwd+bwd of all {n} heads" if n == pr.heads else
+                       f"fwd+bwd of {n} of {pr.heads} heads (b=0, h<{n})") +
+                      f" at S={pr.seq_q}: the plain C++ fp64 oracle, OpenMP over heads; "
+                      f"algorithmic flops 14*D per visible pair",
             "single_thread_seconds": single}
 
 
@@ -383,7 +383,7 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload id 1..5 (5 = the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="heads in the CPU-baseline sample (0: one per host thread)")
+                    help="heads in the CPU-baseline sample (0: all of them)")
     ap.add_argument("--more", default="1,2,3,4",
                     help="comma-separated workload ids whose forward is also timed and reported "
                          "under 'workloads' (empty: none)")
