@@ -333,10 +333,8 @@ def bench_config(cid: int, steps: int, warmup: int) -> dict:
     def fwd(t):
         plan.fwd(t[0], t[1], t[2], t[4], t[5])
 
-    def bwd(t):
-        plan.bwd_prep(t[4], t[3])
-        plan.bwd_main(t[0], t[1], t[2], t[5], t[3], t[7], t[8])
-        plan.bwd_post(t[0], t[1], t[2], t[5], t[3], t[6])
+    def bwd(t):   # fa_bwd, the whole backward (its steps, or one pass for short query blocks)
+        plan.bwd(t[0], t[1], t[2], t[4], t[5], t[3], t[6], t[7], t[8])
 
     def timed(fn, alternate):
         for i in range(warmup):

@@ -645,7 +645,11 @@ def test_tile_switch_and_launch_log(monkeypatch, capfd, tile, Sq, want):
     assert line and want in line[-1] and "masks=padding" in line[-1], err
     check_bwd(pr, o, lse)
     err = capfd.readouterr().err
-    assert "[libfa] fa_bwd_main" in err and "[libfa] fa_bwd_post" in err
+    if Sq <= 32 and tile in ("auto", "short"):
+        assert "[libfa] fa_bwd: " in err and "bwd_short_kernel" in err, err
+        assert "[libfa] fa_bwd_main" not in err, err
+    else:
+        assert "[libfa] fa_bwd_main" in err and "[libfa] fa_bwd_post" in err, err
 
 
 # ----------------------------------------------------------------------------------

@@ -397,9 +397,10 @@ def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, *, heads: int, layout: str = "B
 
 
 class Plan:
-    """A prepared problem: the struct is built once and the four device calls
-    (fwd; bwd prep = row terms, bwd main = dK/dV, bwd post = dQ) can be issued
-    repeatedly, e.g. by a benchmark that brackets each call with events."""
+    """A prepared problem: the struct is built once and the device calls (fwd;
+    the whole backward; or its steps: bwd prep = row terms, bwd main = dK/dV,
+    bwd post = dQ) can be issued repeatedly, e.g. by a benchmark that brackets
+    each call with events."""
 
     def __init__(self, q, k, *, heads: int, layout: str = "BNSD", **kw):
         self.p, self._keep = make_problem(q, k, heads=heads, layout=layout, **kw)
@@ -411,6 +412,11 @@ class Plan:
     def fwd(self, q, k, v, o, lse):
         _check(lib.fa_fwd(self._pp, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream()),
                "fa_fwd")
+
+    def bwd(self, q, k, v, o, lse, do, dq, dk, dv):
+        _check(lib.fa_bwd(self._pp, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(self.ws), self.ws.numel(), _stream()),
+               "fa_bwd")
 
     def bwd_prep(self, o, do):
         _check(lib.fa_bwd_prep(self._pp, _ptr(o), _ptr(do), _ptr(self.ws), self.ws.numel(),

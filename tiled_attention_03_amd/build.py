@@ -15,7 +15,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.hip", "fa_f32.hip", "fa_fwd.hip", "fa_fwd_bf16_d64.hip", "fa_fwd_bf16_d128.hip",
-           "fa_fwd_f16_d64.hip", "fa_fwd_f16_d128.hip", "fa_bwd.hip", "fa_bwd_split.hip", "fa_maxsim.hip",
+           "fa_fwd_f16_d64.hip", "fa_fwd_f16_d128.hip", "fa_bwd.hip", "fa_bwd_split.hip", "fa_bwd_short.hip", "fa_maxsim.hip",
            "fa_fwd_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -333,6 +333,14 @@ fa_status fa_bwd(const fa_problem *p, const void *q, const void *k, const void *
     return FA_ERR_INVALID_ARG;
   if ((st = workspace_ok(p, workspace, workspace_bytes)) != FA_OK) return st;
   if ((st = fa_bwd_prep(p, o, dout, workspace, workspace_bytes, stream)) != FA_OK) return st;
+  {
+    // short query blocks: dQ, dK and dV in one pass per (batch, head)
+    Params r = make_params(p);
+    r.q = q; r.k = k; r.v = v; r.lse = (float *)lse; r.dout = dout;
+    r.dq = dq; r.dk = dk; r.dv = dv;
+    bind_workspace(r, workspace);
+    if (bwd_short_fits(r, p->dtype)) return hip_status(launch_bwd_short(r, p->dtype, stream));
+  }
   if ((st = fa_bwd_main(p, q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, stream)) != FA_OK)
     return st;
   return fa_bwd_post(p, q, k, v, lse, dout, dq, workspace, workspace_bytes, stream);

@@ -12,12 +12,14 @@ namespace fa {
 // Run-time switches read from the environment at each call (host side only):
 //   FA_LOG=1   every call prints the kernel instance it launches and its grid
 //              on stderr (one line per launch);
-//   FA_TILE=   forward workgroup shape, for sweeps: "auto" (default: the
-//              short-query kernel where it applies, else one-wave workgroups
-//              for S_q <= 32 and four-wave ones otherwise), "short" (the same
-//              as auto), "wg4" (four-wave workgroups for every S_q), "wg1"
-//              (one-wave list-based workgroups for every S_q whose key range
-//              fits their lists).
+//   FA_TILE=   workgroup shape, for sweeps: "auto" (default: the short-query
+//              forward and backward where they apply, else one-wave forward
+//              workgroups for S_q <= 32 and four-wave ones otherwise),
+//              "short" (the same as auto), "wg4" (four-wave forward
+//              workgroups for every S_q, and the key and query passes for
+//              every backward), "wg1" (one-wave list-based forward
+//              workgroups for every S_q whose key range fits their lists,
+//              and the key and query passes for every backward).
 // Unknown FA_TILE values count as "auto".  The choice never changes results
 // beyond rounding order.
 enum { kTileAuto = 0, kTileWg4 = 1, kTileWg1 = 2, kTileShort = 3 };
@@ -55,6 +57,12 @@ hipError_t launch_bwd_q_mfma(const Params &p, int dtype, hipStream_t s);
 // memset node, so that it behaves inside captured graphs.
 hipError_t launch_zero_words(void *dst, int64_t n_words, hipStream_t s);
 hipError_t launch_bwd_q_f32(const Params &p, hipStream_t s);
+// Backward for short query blocks (S_q <= 32, causal / padding masks, ALiBi
+// or no bias, no dropout, gradients in the input dtype): dQ, dK and dV in one
+// pass per (batch, head).  Selected by fa_bwd when bwd_short_fits() and
+// FA_TILE is "auto" or "short"; the step entry points keep their own passes.
+bool bwd_short_fits(const Params &p, int dtype);
+hipError_t launch_bwd_short(const Params &p, int dtype, hipStream_t s);
 
 // MaxSim late-interaction scores (see fa_maxsim in include/fa.h).
 struct MaxSimParams {
