@@ -47,9 +47,15 @@ makes the score -inf as soon as one query token is padding; here that row's
 max is reported as -inf but left out of the sum (the divisor stays L_q, as
 printed).
 
-Every function is pinned by ``tests/test_oracle_pins.py`` (brute force,
-closed forms, invariants, finite differences, a library attention routine
-on sliced problems).  Nothing here is "parity unpinned".
+Every function is pinned: the core by ``tests/test_oracle_pins.py`` (brute
+force, closed forms, invariants, finite differences, a library attention
+routine on sliced problems), the problem wrappers ``problem_masks``,
+``problem_fwd`` and ``problem_bwd`` by ``tests/test_oracle_problem_pins.py``
+(BSH against BNSD, each mask and bias field changing exactly the rows it
+should, the dropout fields reaching the core, the bias gradient against
+central differences).  Nothing here is "parity unpinned".  The plain C++
+fp64 oracle in ``oracle/fa_ref.cpp`` (``oracle.cpp``) computes the same
+definition independently and is pinned by ``tests/test_oracle_cpp.py``.
 """
 from __future__ import annotations
 
