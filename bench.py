@@ -394,7 +394,14 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--workloads-only", action="store_true",
+                    help="only time the --more workloads (20 calls each after 5 warm-up) and "
+                         "print their records; no headline step (for profiling runs)")
     args = ap.parse_args()
+    if args.workloads_only:
+        print(json.dumps({"workloads": {f"c{c}": bench_config(int(c), 20, 5)
+                                        for c in args.more.split(",") if c}}))
+        return
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
