@@ -98,6 +98,12 @@
  * Outputs are valid once the stream reaches that point.  The library keeps
  * no mutable global state; calls are thread-safe.  Two calls that write the
  * same buffers on different streams race, as with any stream work.
+ *
+ * Environment (read at every call; for diagnostics and sweeps): FA_LOG=1
+ * prints each launch's kernel instance and grid on stderr; FA_TILE=auto
+ * (default) | short | wg4 | wg1 picks the workgroup shape: wg4 and wg1 turn
+ * off the kernels for short query blocks (S_q <= 32).  Results agree with
+ * the definition either way, to rounding order.
  */
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
