@@ -555,14 +555,15 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float off = lane_off[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4];
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float x = exp2_fast(fmaf(s[rb][kb][r], cs, off));
             s[rb][kb][r] = x;
-            part[r & 3] += x;
+            if (kb == 0 && r < 4) part[r] = x;   // (0 + x is not folded away: -0)
+            else part[r & 3] += x;
           }
         l_run[rb] = l_run[rb] * alpha[rb] + ((part[0] + part[1]) + (part[2] + part[3]));
         if (DROP) {
@@ -728,7 +729,6 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb) sn[rb][kb] = s_init;
-      part[rb][0] = part[rb][1] = part[rb][2] = part[rb][3] = 0.f;
     }
     u32x4 va[NC][DB];
 #pragma unroll
@@ -750,7 +750,8 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         const int rb = e / (16 * KBN), kb = (e / 16) % KBN, r = e % 16;
         const float x = exp2_fast(fmaf(s[rb][kb][r], c_log2, kb ? offk[rb] : off[rb]));
         s[rb][kb][r] = x;
-        part[rb][r & 3] += x;   // four short sum chains instead of one long one
+        if (kb == 0 && r < 4) part[rb][r] = x;   // four short sum chains
+        else part[rb][r & 3] += x;
       }
       __builtin_amdgcn_sched_barrier(0x0004);
     }
@@ -758,6 +759,9 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l_run[rb] = l_run[rb] * alpha[rb] + ((part[rb][0] + part[rb][1]) + (part[rb][2] + part[rb][3]));
+      // pins the sum here: left free, the compiler sinks one step's sum into
+      // the next step's head, a serial chain ahead of its first products
+      asm volatile("" : "+v"(l_run[rb]));
 #pragma unroll
       for (int c = 0; c < NC; ++c) pk[rb][c] = pack8<T>(s[rb][c >> 1], 8 * (c & 1));
     }
