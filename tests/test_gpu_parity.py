@@ -605,6 +605,9 @@ SHORT = [
     (2, 3, 29, 96, 128, torch.bfloat16, "BSH", "none", 3407),
     (1, 2, 32, 1, 64, torch.bfloat16, "BNSD", "none", 3408),
     (2, 2, 24, 500, 64, torch.bfloat16, "BNSD", "explicit", 3409),
+    (2, 2, 32, 2048, 128, torch.float16, "BSH", "alibi+padding", 3411),
+    (2, 3, 32, 1000, 64, torch.bfloat16, "BNSD", "causal+alibi+holes", 3412),
+    (3, 2, 9, 300, 128, torch.bfloat16, "BNSD", "holes", 3413),
 ]
 
 

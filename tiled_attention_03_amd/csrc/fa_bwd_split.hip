@@ -327,12 +327,17 @@ __global__ __launch_bounds__(2 * NPW * 64, 1) void bwd_kv_split_kernel(Params p,
         dpn = Mfma<T>::mac(ga[t], vf[t], dpn);
 #pragma unroll
         for (int r = PRE + t * (16 - PRE) / KS; r < PRE + (t + 1) * (16 - PRE) / KS; ++r) elem(r);
+        // the first half of P^T and dS^T goes to the exchange slot as soon as
+        // its elements are done, so the step's tail only writes the second
+        if (PRE + t * (16 - PRE) / KS < 8 && PRE + (t + 1) * (16 - PRE) / KS >= 8) {
+          u32x4 *x = xbuf(bi) + l;
+          x[0] = pack8<T>(s, 0);
+          x[128] = pack8<T>(dp, 0);
+        }
         __builtin_amdgcn_sched_barrier(0x0004);
       }
       u32x4 *x = xbuf(bi) + l;
-      x[0] = pack8<T>(s, 0);
       x[64] = pack8<T>(s, 8);
-      x[128] = pack8<T>(dp, 0);
       x[192] = pack8<T>(dp, 8);
       __builtin_amdgcn_sched_barrier(0);
       const bool more = n + 3 < nb;
