@@ -87,7 +87,9 @@
  * maximum over raw scores before scaling), keep_prob < 1 with F32 or fp8,
  * dpse with F32 or fp8, a
  * head_dim the kernels do not cover (F16/BF16: 64 or 128; F32: 32, 64 or
- * 128).  FA_ERR_WORKSPACE: workspace
+ * 128), sizes past the kernels' 32-bit counters (B*H or H*D above
+ * 2^31 - 1, one (batch, head) span of Q- or K-shaped rows of 2 GiB or more,
+ * B*H*S_q above 2^31 - 1 rows).  FA_ERR_WORKSPACE: workspace
  * too small.  FA_ERR_HIP: a HIP launch reported an error.
  * Sizes of zero are allowed: B or H == 0 is a no-op; S_q == 0 makes the
  * forward and the steps other than fa_bwd_main a no-op, while fa_bwd and

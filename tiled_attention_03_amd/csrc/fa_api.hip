@@ -91,18 +91,20 @@ fa_status check_problem(const fa_problem *p) {
   if (p->mask_flags & ~known) return FA_ERR_INVALID_ARG;
   if (p->pse_kind != FA_PSE_NONE && p->pse_kind != FA_PSE_ALIBI && p->pse_kind != FA_PSE_DENSE)
     return FA_ERR_INVALID_ARG;
-  // one (batch, head) span of Q/K-shaped tensors must stay below 2 GiB: the
-  // kernels address it with 32-bit byte offsets
+  // sizes whose indices must fit the kernels' 32-bit counters, each product
+  // bounded before it enters the next, so none leaves 64-bit range: B·H and
+  // H·D, then one (batch, head) span of Q/K-shaped tensors below 2 GiB (the
+  // kernels address it with 32-bit byte offsets), then B·H·S_q rows
+  const int64_t bh = (int64_t)p->batch * p->head_num;
+  const int64_t hd = (int64_t)p->head_num * p->head_dim;
+  if (bh > INT32_MAX || hd > INT32_MAX) return FA_ERR_UNSUPPORTED;
   {
     const int64_t es = p->dtype == FA_F32 ? 4 : 2;
-    const int64_t hd = (int64_t)p->head_num * p->head_dim;
     const int64_t rs = p->layout == FA_BSH ? hd : p->head_dim;
-    const int64_t span_q = ((int64_t)p->seq_q * rs) * es, span_k = ((int64_t)p->seq_k * rs) * es;
-    if (span_q >= ((int64_t)1 << 31) || span_k >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+    const int64_t lim = ((int64_t)1 << 31) / es;   // elements
+    if ((int64_t)p->seq_q * rs >= lim || (int64_t)p->seq_k * rs >= lim) return FA_ERR_UNSUPPORTED;
   }
-  // sizes whose indices must fit the kernels' 32-bit row counters
-  const int64_t rows_q = (int64_t)p->batch * p->head_num * p->seq_q;
-  if (rows_q > INT32_MAX || (int64_t)p->head_num * p->head_dim > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (bh * p->seq_q > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (empty_problem(p)) return FA_OK;
   if (p->mask_flags & FA_MASK_EXPLICIT) {
     if (!p->explicit_mask) return FA_ERR_INVALID_ARG;
@@ -227,7 +229,11 @@ extern "C" {
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
 const char *fa_status_str(fa_status s) {
-  switch (s) {
+  // a C caller may pass any int; read it as one (a load of an out-of-range
+  // value as the enum type would be undefined in C++)
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -406,7 +412,7 @@ fa_status fa_maxsim(const fa_maxsim_problem *p, const void *q, const void *d, fl
   if (p->dim % 128 != 0 || p->dim > kMaxSimMaxDim || p->len_d > kMaxSimMaxDocs)
     return FA_ERR_UNSUPPORTED;
   const int64_t b_pad = ((int64_t)p->batch + 7) / 8 * 8;
-  if (b_pad * ((p->len_q + 31) / 32) > INT32_MAX || (int64_t)p->batch * p->len_q > INT32_MAX)
+  if (b_pad * (((int64_t)p->len_q + 31) / 32) > INT32_MAX || (int64_t)p->batch * p->len_q > INT32_MAX)
     return FA_ERR_UNSUPPORTED;
   if (p->batch == 0) return FA_OK;
   if (!score || ((uintptr_t)score & 3u)) return FA_ERR_INVALID_ARG;
