@@ -49,7 +49,9 @@ printed).
 
 Every function is pinned: the core by ``tests/test_oracle_pins.py`` (brute
 force, closed forms, invariants, finite differences, a library attention
-routine on sliced problems), the problem wrappers ``problem_masks``,
+routine on sliced problems; the row-restricted :func:`attention_rows`, which
+full-size GPU checks use on sampled rows, against the brute force and torch
+autograd), the problem wrappers ``problem_masks``,
 ``problem_fwd`` and ``problem_bwd`` by ``tests/test_oracle_problem_pins.py``
 (BSH against BNSD, each mask and bias field changing exactly the rows it
 should, the dropout fields reaching the core, the bias gradient against
@@ -84,8 +86,9 @@ def bnsd_to_bsh(x: np.ndarray) -> np.ndarray:
 
 def allowed(b, h, Sq, Sk, *, causal=False, explicit_mask=None, q_modality=None,
             k_modality=None, modality_allow=None, modality_allow_diag=False,
-            key_valid=None) -> np.ndarray:
-    """Boolean [Sq, Sk]: may query i of head (b, h) attend to key j.
+            key_valid=None, rows=None) -> np.ndarray:
+    """Boolean [Sq, Sk]: may query i of head (b, h) attend to key j.  With
+    ``rows`` (query indices) only those rows are formed, [len(rows), Sk].
 
     The mask kinds combine by AND:
     * causal: the lower triangle ``tril`` including the diagonal, j <= i
@@ -96,57 +99,65 @@ def allowed(b, h, Sq, Sk, *, causal=False, explicit_mask=None, q_modality=None,
       i == j (the multimodal page's default rule keeps the diagonal);
     * padding: key j of sample b is a real token (retrieval page doc_mask).
     """
-    ok = np.ones((Sq, Sk), dtype=bool)
+    r = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    j = np.arange(Sk)
+    ok = np.ones((len(r), Sk), dtype=bool)
     if causal:
-        ok &= np.tril(np.ones((Sq, Sk), dtype=bool))
+        ok &= j[None, :] <= r[:, None]    # tril, the diagonal included
     if explicit_mask is not None:
         em = np.asarray(explicit_mask, dtype=bool)
         if em.ndim == 2:                  # [Sq, Sk]
             em = em[None, None]
         elif em.ndim == 3:                # [B, Sq, Sk], shared by every head
             em = em[:, None]
-        ok &= em[b if em.shape[0] > 1 else 0, h if em.shape[1] > 1 else 0]
+        ok &= em[b if em.shape[0] > 1 else 0, h if em.shape[1] > 1 else 0][r]
     if q_modality is not None:
         allow = np.asarray(modality_allow, dtype=bool)
-        qm = np.asarray(q_modality)[b].astype(np.int64)
+        qm = np.asarray(q_modality)[b].astype(np.int64)[r]
         km = np.asarray(k_modality)[b].astype(np.int64)
         m = allow[qm[:, None], km[None, :]]
         if modality_allow_diag:
-            m = m | np.eye(Sq, Sk, dtype=bool)
+            m = m | (j[None, :] == r[:, None])
         ok &= m
     if key_valid is not None:
         ok &= np.asarray(key_valid, dtype=bool)[b][None, :]
     return ok
 
 
-def bias(b, h, Sq, Sk, *, pse=None, alibi_slopes=None) -> np.ndarray | None:
-    """float64 [Sq, Sk] additive bias for head (b, h), or None.
+def bias(b, h, Sq, Sk, *, pse=None, alibi_slopes=None, rows=None) -> np.ndarray | None:
+    """float64 [Sq, Sk] additive bias for head (b, h), or None (with ``rows``,
+    only those query rows).
 
     ``pse`` is a dense tensor broadcastable to [B, H, Sq, Sk]; ALiBi uses
     -slope_h * |i - j| with the caller's slope values (upcast exactly)."""
+    r = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = None
     if pse is not None:
         p = np.asarray(pse, dtype=np.float64)
         p = p[b if p.shape[0] > 1 else 0, h if p.shape[1] > 1 else 0]
-        out = np.broadcast_to(p, (Sq, Sk)).astype(np.float64)
+        out = np.broadcast_to(p, (Sq, Sk))[r].astype(np.float64)
     if alibi_slopes is not None:
         slope = float(np.asarray(alibi_slopes, dtype=np.float64)[h])
-        i = np.arange(Sq, dtype=np.float64)[:, None]
+        i = r.astype(np.float64)[:, None]
         j = np.arange(Sk, dtype=np.float64)[None, :]
         a = -slope * np.abs(i - j)
         out = a if out is None else out + a
     return out
 
 
-def head_scores(q, k, scale, b, h, masks: dict) -> np.ndarray:
+def head_scores(q, k, scale, b, h, masks: dict, rows=None) -> np.ndarray:
     """Scaled scores plus bias for head (b, h), with disallowed entries set to
-    exactly -inf.  ``q`` [B,H,Sq,D] and ``k`` [B,H,Sk,D] are float64."""
+    exactly -inf.  ``q`` [B,H,Sq,D] and ``k`` [B,H,Sk,D] are float64.  With
+    ``rows`` (query indices) only those rows of the score matrix."""
     Sq, Sk = q.shape[2], k.shape[2]
-    s = scale * (q[b, h] @ k[b, h].T)
-    bb = bias(b, h, Sq, Sk, pse=masks.get("pse"), alibi_slopes=masks.get("alibi_slopes"))
+    qr = q[b, h] if rows is None else q[b, h][np.asarray(rows, dtype=np.int64)]
+    s = scale * (qr @ k[b, h].T)
+    bb = bias(b, h, Sq, Sk, pse=masks.get("pse"), alibi_slopes=masks.get("alibi_slopes"),
+              rows=rows)
     if bb is not None:
         s = s + bb
-    ok = allowed(b, h, Sq, Sk, **{key: masks[key] for key in _MASK_KEYS if key in masks})
+    ok = allowed(b, h, Sq, Sk, rows=rows,
+                 **{key: masks[key] for key in _MASK_KEYS if key in masks})
     return np.where(ok, s, -np.inf)
 
 
@@ -312,6 +323,25 @@ def attention_bwd(q, k, v, do, scale, keep_prob=1.0, dropout_seed=0, return_dbia
             if dbias is not None:
                 dbias[b, h] = dS
     return (dq, dk, dv) if dbias is None else (dq, dk, dv, dbias)
+
+
+def attention_rows(q, k, v, do, scale, rows, b=0, h=0, **masks):
+    """O, LSE and dQ of the query rows ``rows`` of head (b, h) only (float64,
+    [len(rows), D], [len(rows)], [len(rows), D]), BNSD inputs, no dropout.
+
+    Each of these is a function of its own row of scores: P_i is the softmax
+    of row i, O_i = sum_j P_ij v_j, dP_ij = dO_i . v_j, D_i = sum_j P_ij dP_ij,
+    dQ_i = scale sum_j P_ij (dP_ij - D_i) k_j -- the same quantities as
+    :func:`attention_fwd` and :func:`attention_bwd` form for every row, here
+    for a few rows of a problem too large to form whole."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    P, lse = softmax_rows(head_scores(q, k, scale, b, h, _masks(masks), rows=rows))
+    r = np.asarray(rows, dtype=np.int64)
+    O = P @ v[b, h]
+    dP = do[b, h][r] @ v[b, h].T
+    Dl = (P * dP).sum(axis=1)
+    dQ = scale * ((P * (dP - Dl[:, None])) @ k[b, h])
+    return O, lse, dQ
 
 
 def problem_masks(p) -> dict:

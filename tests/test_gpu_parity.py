@@ -58,6 +58,28 @@ def test_long_sequence_sampled_heads():
         assert_close("dV", slice_out(dv, pr, h), rv, pr.dtype)
 
 
+def test_long_sequence_every_head_sampled_rows():
+    """Every head of the long workload at full size, in the launch configuration
+    the benchmark times: O, LSE and dQ of sampled query rows (tile edges, the
+    first and last rows, and seeded random ones) against the row-restricted
+    oracle, which forms only those rows of each head's score matrix."""
+    pr = inputs.config(5)
+    print(f"\n{pr.name}")
+    o, lse = gpu_fwd(pr)
+    dq, _, _ = gpu_bwd(pr, o, lse)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, 2047, 4096, 6143, 8190, 8191]
+    rng = np.random.default_rng(5151)
+    for h in range(pr.heads):
+        rows = np.array(edges + sorted(rng.choice(pr.seq_q, 6, replace=False).tolist()))
+        O, L, dQ = oracle.attention_rows(pr.q[:, h:h + 1], pr.k[:, h:h + 1], pr.v[:, h:h + 1],
+                                         pr.do[:, h:h + 1], pr.scale, rows, causal=pr.causal,
+                                         alibi_slopes=pr.alibi_slopes[h:h + 1])
+        idx = torch.tensor(rows, device=o.device)
+        assert_close(f"O h{h}", o[0, h].index_select(0, idx), O, pr.dtype)
+        assert_lse(lse[0, h].index_select(0, idx), L)
+        assert_close(f"dQ h{h}", dq[0, h].index_select(0, idx), dQ, pr.dtype)
+
+
 def test_long_sequence_forward_more_heads():
     pr = inputs.config(5, with_do=False)
     o, lse = gpu_fwd(pr)

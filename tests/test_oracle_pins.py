@@ -743,3 +743,61 @@ def test_e4m3_decode_all_codes_against_torch():
     # a few values written out: 1.0, the largest normal, the smallest subnormal, -2
     assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
     assert got[0xC0] == -2.0
+
+
+# ----------------------------------------------------------------------------------
+# the row-restricted oracle (full-size sampled checks) against independent references
+
+@pytest.mark.parametrize("name,masks,rule,bias_fn", CASES, ids=[c[0] for c in CASES])
+def test_attention_rows_against_bruteforce_and_torch(name, masks, rule, bias_fn):
+    """attention_rows on a subset of rows (in any order, repeats allowed) equals the
+    term-by-term brute force (O, LSE) and torch autograd of the same masked,
+    biased softmax in float64 (dQ) on those rows."""
+    B, H, Sq, Sk = SHAPE
+    D = 5
+    q, k, v, do = rnd((B, H, Sq, D), 121), rnd((B, H, Sk, D), 122), rnd((B, H, Sk, D), 123), \
+        rnd((B, H, Sq, D), 124)
+    rows = np.array([6, 0, 3, 3, 5])
+    for b in range(B):
+        for h in range(H):
+            O, L, dQ = oracle.attention_rows(q, k, v, do, 0.45, rows, b, h, **masks)
+            NO, NL = naive_attention(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), 0.45,
+                                     lambda i, j: rule(b, h, i, j),
+                                     None if bias_fn is None else lambda i, j: bias_fn(b, h, i, j))
+            for n, i in enumerate(rows):
+                if NL[i] == -math.inf:
+                    assert L[n] == -math.inf and np.all(O[n] == 0) and np.all(dQ[n] == 0)
+                    continue
+                np.testing.assert_allclose(O[n], NO[i], atol=1e-13)
+                assert abs(L[n] - NL[i]) < 1e-13
+            # dQ of the live rows: torch autograd of the same function of q
+            add = np.array([[(bias_fn(b, h, i, j) if bias_fn else 0.0) if rule(b, h, i, j)
+                             else -np.inf for j in range(Sk)] for i in range(Sq)])
+            live = np.isfinite(add).any(axis=-1)
+            tq = torch.tensor(q[b, h], requires_grad=True)
+            s = 0.45 * tq @ torch.tensor(k[b, h]).T + torch.tensor(add)
+            p = torch.softmax(s, dim=-1)
+            out = torch.nan_to_num(p @ torch.tensor(v[b, h]))
+            (out * torch.tensor(do[b, h] * live[:, None])).sum().backward()
+            for n, i in enumerate(rows):
+                if live[i]:
+                    np.testing.assert_allclose(dQ[n], tq.grad.numpy()[i], atol=1e-12)
+
+
+def test_attention_rows_match_the_whole_head_forms():
+    """Every row at once equals attention_fwd / attention_bwd of the whole problem."""
+    B, H, Sq, Sk = SHAPE
+    D = 4
+    q, k, v, do = rnd((B, H, Sq, D), 131), rnd((B, H, Sk, D), 132), rnd((B, H, Sk, D), 133), \
+        rnd((B, H, Sq, D), 134)
+    masks = CASES[-1][1]
+    O, L = oracle.attention_fwd(q, k, v, 0.3, **masks)
+    dq, _, _ = oracle.attention_bwd(q, k, v, do, 0.3, **masks)
+    for b in range(B):
+        for h in range(H):
+            Or, Lr, dQr = oracle.attention_rows(q, k, v, do, 0.3, np.arange(Sq), b, h, **masks)
+            np.testing.assert_allclose(Or, O[b, h], atol=1e-14)
+            np.testing.assert_array_equal(np.isneginf(Lr), np.isneginf(L[b, h]))
+            fin = np.isfinite(Lr)
+            np.testing.assert_allclose(Lr[fin], L[b, h][fin], atol=1e-14)
+            np.testing.assert_allclose(dQr, dq[b, h], atol=1e-13)
