@@ -636,6 +636,11 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
     // needs no per-element work (an explicit mask always takes the per-element
     // code)
     bool skip = false;
+    // padding and modality rules for this lane's row against the tile's keys,
+    // from the same votes (lane l votes for key k0 + l): bit jj says key
+    // k0 + jj exists, is valid and its modality is allowed to the row (or it
+    // is the row's own position under the diagonal rule)
+    uint64_t kmask = ~0ull;
     if (GEN && f_elem) {
       static_assert(KBQ == 64, "one key per lane");
       const int j = k0 + l;
@@ -643,11 +648,21 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
       bool kv = in;
       if (in && (flags & FA_MASK_PADDING)) kv = p.key_valid[(int64_t)b * p.Sk + j] != 0;
       const uint64_t kvm = __ballot(kv);
+      kmask = kvm;
       bool any = kvm != 0;
       bool full = !(flags & FA_MASK_EXPLICIT) && kvm == __ballot(in);
       if (flags & FA_MASK_MODALITY) {
         const int mk = kv ? p.kmod[(int64_t)b * p.Sk + j] : -1;
         const int mq = my_i < p.Sq ? p.qmod[(int64_t)b * p.Sq + my_i] : -1;
+        const uint32_t my_row = mq >= 0 ? (uint32_t)(p.allow_bits >> (8 * mq)) & 0xffu : 0u;
+        uint64_t mm = 0ull;
+        for (int c = 0; c < p.num_modalities; ++c) {
+          const uint64_t kc = __ballot(mk == c);
+          if (kc != 0ull && ((my_row >> c) & 1u)) mm |= kc;
+        }
+        const int d = my_i - k0;
+        if (p.allow_diag && d >= 0 && d < KBQ) mm |= 1ull << d;
+        kmask = kvm & mm;
         bool some = false, all = true;
         for (int a = 0; a < p.num_modalities; ++a) {
           if (!__ballot(mq == a)) continue;
@@ -739,11 +754,15 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(Params p, int n_qtiles) {
             for (int rr = 0; rr < 4; ++rr)
               keep[rr] = dropout_keep4(p, b, h, my_i, k0 + 32 * jb + 8 * rr + 4 * g);
           }
+          // the lane's keys of this block sit at bits 8 (r / 4) + r % 4 of kw
+          const uint32_t kw = (uint32_t)((kmask >> (4 * g)) >> (32 * jb));
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-            bool ok = j < p.Sk && my_i < p.Sq;
-            if (ok) ok = allowed_elem(p, b, h, my_i, j);
+            bool ok = j < p.Sk && my_i < p.Sq && ((kw >> (8 * (r >> 2) + (r & 3))) & 1u);
+            if (causal) ok = ok && j <= my_i;
+            if (ok && (flags & FA_MASK_EXPLICIT))
+              ok = p.em[(int64_t)b * p.em_sb + (int64_t)h * p.em_sh + (int64_t)my_i * p.em_sq + j] != 0;
             float pr = 0.f;
             if (ok) {
               float t = s[r] * c_log2;

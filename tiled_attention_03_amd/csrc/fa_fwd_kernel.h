@@ -524,17 +524,64 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         }
       } else {
         cs = 1.f;
+        // padding and modality rules of the tile's keys for this lane's rows,
+        // from wave votes (lane l votes for key k0 + l): bit jj of kmask[rb]
+        // says key k0 + jj exists, is valid and its modality is allowed to the
+        // row (or it is the row's own position under the diagonal rule)
+        uint64_t kmask[RB];
+        const bool vote = f_pad || f_mod;
+        if (vote) {
+          const int jl = k0 + l;
+          const bool kin = l < BN && jl < p.Sk;
+          bool kv = kin;
+          if (f_pad && kin) kv = p.key_valid[(int64_t)b * p.Sk + jl] != 0;
+          const uint64_t vmask = __ballot(kv);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) kmask[rb] = f_mod ? 0ull : vmask;
+          if (f_mod) {
+            // modalities this lane's rows may attend (read per tile rather than
+            // held through the kernel, which has no register to spare)
+            uint32_t row_allow[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const int i = my_i[rb];
+              const int mq = i < p.Sq ? p.qmod[(int64_t)b * p.Sq + i] : -1;
+              row_allow[rb] = mq >= 0 ? (uint32_t)(p.allow_bits >> (8 * mq)) & 0xffu : 0u;
+            }
+            const int mk = kin ? p.kmod[(int64_t)b * p.Sk + jl] : -1;
+            for (int a = 0; a < p.num_modalities; ++a) {
+              const uint64_t km = __ballot(mk == a);
+              if (km == 0ull) continue;
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+                if ((row_allow[rb] >> a) & 1u) kmask[rb] |= km;
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const int d = my_i[rb] - k0;
+              if (p.allow_diag && d >= 0 && d < BN) kmask[rb] |= 1ull << d;
+              kmask[rb] &= vmask;
+            }
+          }
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int i = my_i[rb];
+          // the lane's keys of 32-key block kb sit at bits 8 (r / 4) + r % 4
+          // of word kb once the mask is shifted by the lane half's 4 g
+          const uint64_t kmg = vote ? kmask[rb] >> (4 * g) : 0ull;
 #pragma unroll
           for (int kb = 0; kb < KBN; ++kb) {
+            const uint32_t kw = (uint32_t)(kmg >> (32 * kb));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
               float t = s[rb][kb][r] * c_log2;
               bool ok = j < p.Sk && i < p.Sq;
-              if (ok) ok = allowed_elem(p, b, h, i, j);
+              if (vote) ok = ok && ((kw >> (8 * (r >> 2) + (r & 3))) & 1u);
+              if (causal) ok = ok && j <= i;
+              if (f_exp && ok)
+                ok = p.em[(int64_t)b * p.em_sb + (int64_t)h * p.em_sh + (int64_t)i * p.em_sq + j] != 0;
               if (ok) {
                 if (alibi) t -= sl2 * fabsf((float)(i - j));
                 else if (dense) t += dense_bias(p, b, h, i, j) * kLog2e;
