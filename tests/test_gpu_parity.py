@@ -276,6 +276,28 @@ def test_large_scores_exercise_running_max(D):
     check_fwd(pr)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("mask", ["none", "causal+alibi"])
+def test_score_spike_in_a_late_tile(D, dtype, mask):
+    """One key of head 0 (key 3, in the tile the forward visits last outside
+    the causal band) scores about 180 base-2 units above every other key of
+    the head: after the first tiles, an exponential taken against the running
+    reference would overflow, so the workgroups of head 0 that meet it late
+    must redo their tiles with the row max taken on each.  Head 1 is plain."""
+    pr = make_case(1, 2, 300, 600, D, dtype, "BNSD", mask, 980 + D)
+    if "causal" in mask:
+        pr = make_case(1, 2, 600, 600, D, dtype, "BNSD", mask, 980 + D)
+    g = torch.Generator().manual_seed(981 + D)
+    u = torch.randn(D, generator=g)
+    q, k = pr.q.float(), pr.k.float()
+    q[0, 0] += u
+    k[0, 0, 3] = 16.0 * u
+    pr.q, pr.k = q.to(dtype), k.to(dtype)
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
 def test_alibi_equals_dense_bias_on_gpu():
     pr = make_case(1, 4, 150, 150, 64, torch.bfloat16, "BNSD", "causal+alibi", 905)
     o1, l1 = gpu_fwd(pr)

@@ -48,7 +48,11 @@
 //     n computes the scores of tile n+1 (MFMA) interleaved with the
 //     exponentials of tile n (VALU), in an order fixed by scheduling fences,
 //     then multiplies P_n by V_n; K tiles are fetched two steps ahead and V
-//     tiles one step ahead.
+//     tiles one step ahead.  Past its first two tiles the phase takes no row
+//     max (the reference stays at an actual score of the row); each lane
+//     checks its share of every tile's sum of exponentials against a bound
+//     far inside the fp32 range, and a workgroup where one does not hold
+//     runs both phases again with the max taken on every tile.
 //
 // Tiles go straight from global memory into LDS (no register staging).  Each
 // of the four tile buffers is its own LDS variable and steps are unrolled in
@@ -73,6 +77,14 @@ namespace {
 constexpr int kMaxTiles = 1024;
 constexpr int kMaxTilesSmall = 128;   // the one-wave (S_q <= 32) instance: less LDS per workgroup
 constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
+// After its first two tiles the fast phase takes no row max: the reference
+// stays where those tiles (and the generic phase) left it, and each lane
+// checks that its share of every tile's exponentials sums to at most kOptMax
+// (so no element exceeds it, and O and l stay far inside the fp32 range).
+// A workgroup where some lane's sum does not runs its tiles again with the
+// max taken on every tile.  The reference is an actual score of the row, so
+// no element that matters can underflow.
+constexpr float kOptMax = 4294967296.f;   // 2^32
 
 template <typename T, int D, int NW, int RB_, int KBN_>
 struct FwdCfg {
@@ -634,28 +646,31 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     vm_wait_barrier();
   };
 
-  if (n_gen > 0) {
-    const int k0t = tile_at(0);
-    load_tile(k0t, K0, Kr);
-    load_tile(k0t, V0, Vr);
-  }
-  vm_wait_barrier();
-  {
+  auto generic_phase = [&]() __attribute__((always_inline)) {
+    if (n_gen > 0) {
+      const int k0t = tile_at(0);
+      load_tile(k0t, K0, Kr);
+      load_tile(k0t, V0, Vr);
+    }
+    vm_wait_barrier();
     int n = 0;
     for (; n + 1 < n_gen; n += 2) {
       generic_step(n, BufIdx<0>{});
       generic_step(n + 1, BufIdx<1>{});
     }
     if (n < n_gen) generic_step(n, BufIdx<0>{});
-  }
+  };
 
-  if constexpr (!LONG) {
+  if constexpr (LONG) {
+    generic_phase();
+  } else {
   // ==== fast phase: software pipeline over list entries n_gen .. n_all-1
   const int n_fast = n_all - n_gen;
   auto ftile = [&](int n) __attribute__((always_inline)) { return tile_at(n_gen + n); };
   // The fast tiles again, pairs of consecutive entries packed in one word, so a
   // step learns both tiles it loads from a single LDS read.  Written here and
-  // read only after the barrier that ends the first fast step's set-up.
+  // read only after the barriers of the generic phase's and the fast phase's
+  // set-up.
   for (int i = tid; i < n_fast; i += C::NT) {
     const uint32_t nxt = i + 1 < n_fast ? (uint32_t)(uint16_t)tlist[n_gen + i + 1] : 0u;
     fpair[i] = (uint32_t)(uint16_t)tlist[n_gen + i] | (nxt << 16);
@@ -679,8 +694,9 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
   // block boundary and the exponentials offset by kb * 32 ash * c_log2.
   // ALiBi without the causal rule folds the whole term per element.
   auto fold_max = [&](f32x16 (&sc)[RB][KBN], int k0, int part, float (&lane_off)[RB],
-                      float (&mx)[RB], auto mask) __attribute__((always_inline)) {
+                      float (&mx)[RB], auto mask, auto opt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask)::value;
+    constexpr bool MX = MASK || !decltype(opt)::value;   // the row max is taken
     const int adir = (causal || k0 + BN - 1 <= q0) ? 1 : -1;
     const float a = fold_pe ? adir * sl2c : 0.f;
     constexpr int NE = 16 * KBN;
@@ -689,7 +705,7 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     for (int rb = 0; rb < RB; ++rb) {
       if (part <= 0) {
         lane_off[rb] = alibi ? adir * sl2 * (float)(k0 + 4 * g - my_i[rb]) : 0.f;
-        mx[rb] = -INFINITY;
+        if (MX) mx[rb] = -INFINITY;
       }
       // element (kb, r) holds key k0 + 4g + c with c = 32kb + 8(r/4) + r%4
       const int lim = causal ? my_i[rb] - k0 - 4 * g : 0x7fffffff;
@@ -698,42 +714,29 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
         if (e < e0 || e >= e1) continue;
         const int kb = e / 16, r = e % 16;
         const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-        if (kb > 0 && r == 0) mx[rb] -= 32.f * ash;   // the block's values lack 32 kb ash
+        if (MX && kb > 0 && r == 0) mx[rb] -= 32.f * ash;   // the block's values lack 32 kb ash
         float v = sc[rb][kb][r];
         if (fold_pe) v = fmaf(a, (float)c, v);
         sc[rb][kb][r] = (MASK && c > lim) ? -INFINITY : v;
-        mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
+        if (MX) mx[rb] = fmaxf(mx[rb], sc[rb][kb][r]);
       }
-      if (part < 0 || part == NC - 1)
+      if (MX && (part < 0 || part == NC - 1))
         mx[rb] = max_lane_pair(fmaf(mx[rb] + (32.f * (KBN - 1)) * ash, c_log2, lane_off[rb]));
     }
   };
 
-  f32x16 sA[RB][KBN], sB[RB][KBN];
-  float loA[RB], mxA[RB], loB[RB], mxB[RB];
-  f32x16 s_init;   // formed here, after the generic phase, which does not use it
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_init[r] = ash * (float)(8 * (r >> 2) + (r & 3));
-  if (n_fast > 0) {
-    const int f0 = ftile(0);
-    load_tile(f0, K0, Kr);
-    load_tile(f0, V0, Vr);
-    if (n_fast > 1) load_tile(ftile(1), K1, Kr);
-  }
-  vm_wait_barrier();
-  if (n_fast > 0) {
-    scores(K0, sA, s_init);
-    fold_max(sA, ftile(0) * BN, -1, loA, mxA, std::bool_constant<true>{});
-  }
-  lds_barrier();   // every wave is done with K0 before the first step refills it
-
   // One step: softmax of tile n (folded scores in s, row max in mx), scores of
   // tile n+1 (into sn) with their fold and max (into lon, mxn), O += P V of
   // tile n.  Buffer parity B: K_{n+1} in K[1-B], V_n in V[B].
+  // OPT (opt): the optimistic form; steps past the first two neither take the
+  // row max nor move the reference, and flag (bad) a lane whose tile sum
+  // passes kOptMax.
+  bool bad = false;
   auto fast_step = [&](int n, auto buf, f32x16 (&s)[RB][KBN], float (&lo)[RB], float (&mx)[RB],
-                       f32x16 (&sn)[RB][KBN], float (&lon)[RB], float (&mxn)[RB], auto mask)
-                       __attribute__((always_inline)) {
+                       f32x16 (&sn)[RB][KBN], float (&lon)[RB], float (&mxn)[RB], auto mask,
+                       auto opt, const f32x16 &s_init) __attribute__((always_inline)) {
     constexpr int B = decltype(buf)::value;
+    constexpr bool OPT = decltype(opt)::value;
     const uint16_t *kn = B ? K0 : K1;   // K of tile n+1
     const uint16_t *vs = B ? V1 : V0;   // V of tile n
     opaque(ro);
@@ -743,7 +746,12 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     if (n + 2 < n_fast) load_tile((int)(pr >> 16), B ? K1 : K0, Kr);
     if (n + 1 < n_fast) load_tile(kt1, B ? V0 : V1, Vr);
     float alpha[RB], off[RB], offk[RB];
-    update_max(mx, alpha);
+    if (!OPT || n <= 1) {   // mx holds the max of tile n (its fold took it)
+      update_max(mx, alpha);
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       off[rb] = lo[rb] - (m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
@@ -805,7 +813,9 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
     u32x4 pk[RB][NC];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      l_run[rb] = l_run[rb] * alpha[rb] + ((part[rb][0] + part[rb][1]) + (part[rb][2] + part[rb][3]));
+      const float tsum_l = (part[rb][0] + part[rb][1]) + (part[rb][2] + part[rb][3]);
+      l_run[rb] = l_run[rb] * alpha[rb] + tsum_l;
+      if (OPT) bad |= tsum_l > kOptMax;
       // pins the sum here: left free, the compiler sinks one step's sum into
       // the next step's head, a serial chain ahead of its first products
       asm volatile("" : "+v"(l_run[rb]));
@@ -823,22 +833,52 @@ void fwd_mfma_kernel(Params p, int n_qtiles) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb][db] = Mfma<T>::mac(va[c][db], pk[rb][c], acc[rb][db]);
-      fold_max(sn, kt1 * BN, c, lon, mxn, mask);
+      fold_max(sn, kt1 * BN, c, lon, mxn, mask, opt);
       __builtin_amdgcn_sched_barrier(0x0004);
     }
     __builtin_amdgcn_s_setprio(0);
     vm_wait_barrier();
   };
-  if (n_fast > 0) {
+  auto fast_phase = [&](auto opt) __attribute__((always_inline)) {
+    f32x16 sA[RB][KBN], sB[RB][KBN];
+    float loA[RB], mxA[RB], loB[RB], mxB[RB];
+    f32x16 s_init;   // formed here, after the generic phase, which does not use it
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_init[r] = ash * (float)(8 * (r >> 2) + (r & 3));
+    const int f0 = ftile(0);
+    load_tile(f0, K0, Kr);
+    load_tile(f0, V0, Vr);
+    if (n_fast > 1) load_tile(ftile(1), K1, Kr);
+    vm_wait_barrier();
+    scores(K0, sA, s_init);
+    fold_max(sA, f0 * BN, -1, loA, mxA, std::bool_constant<true>{}, opt);
+    lds_barrier();   // every wave is done with K0 before the first step refills it
     // causal-band tiles lead the list: tile 0 was folded with the mask above,
     // step 0 folds tile 1 with it, and the steps after it need none
-    fast_step(0, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, std::bool_constant<true>{});
+    constexpr std::bool_constant<false> nomask{};
+    fast_step(0, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, std::bool_constant<true>{}, opt, s_init);
     int n = 1;
     for (; n + 1 < n_fast; n += 2) {
-      fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, std::bool_constant<false>{});
-      fast_step(n + 1, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, std::bool_constant<false>{});
+      fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, nomask, opt, s_init);
+      fast_step(n + 1, BufIdx<0>{}, sA, loA, mxA, sB, loB, mxB, nomask, opt, s_init);
     }
-    if (n < n_fast) fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, std::bool_constant<false>{});
+    if (n < n_fast) fast_step(n, BufIdx<1>{}, sB, loB, mxB, sA, loA, mxA, nomask, opt, s_init);
+  };
+
+  generic_phase();
+  if (n_fast > 0) {
+    fast_phase(std::true_type{});
+    if (__syncthreads_or(bad)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rb][db] = f32x16{};
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+      }
+      generic_phase();
+      fast_phase(std::false_type{});
+    }
   }
   }
 
