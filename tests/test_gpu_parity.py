@@ -332,6 +332,26 @@ def test_score_spike_in_a_late_tile(D, dtype, mask):
     check_bwd(pr, o, lse)
 
 
+@pytest.mark.parametrize("mask", ["none", "padding"])
+def test_short_query_score_spike_in_a_late_tile(mask):
+    """The short-query forward (S_q <= 32): one key of batch 0, head 0 (key 400,
+    tile 12 of 32-key tiles) scores about 180 base-2 units above the rest, so
+    the tiles after the first overflow against the reference the first tile
+    set, and that wave must compute its tiles again with the row max on each."""
+    D = 64
+    pr = make_case(2, 2, 32, 500, D, torch.bfloat16, "BNSD", "none", 990)
+    if mask == "padding":
+        pr.key_valid = torch.arange(500)[None, :] < torch.tensor([[450], [300]])
+    g = torch.Generator().manual_seed(991)
+    u = torch.randn(D, generator=g)
+    q, k = pr.q.float(), pr.k.float()
+    q[0, 0] += u
+    k[0, 0, 400] = 16.0 * u
+    pr.q, pr.k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o, lse = check_fwd(pr)
+    check_bwd(pr, o, lse)
+
+
 def test_alibi_equals_dense_bias_on_gpu():
     pr = make_case(1, 4, 150, 150, 64, torch.bfloat16, "BNSD", "causal+alibi", 905)
     o1, l1 = gpu_fwd(pr)

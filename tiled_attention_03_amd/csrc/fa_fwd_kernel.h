@@ -77,14 +77,9 @@ namespace {
 constexpr int kMaxTiles = 1024;
 constexpr int kMaxTilesSmall = 128;   // the one-wave (S_q <= 32) instance: less LDS per workgroup
 constexpr float kTau = 8.f;     // rescale O only when a row max grows by more than this (log2)
-// After its first two tiles the fast phase takes no row max: the reference
-// stays where those tiles (and the generic phase) left it, and each lane
-// checks that its share of every tile's exponentials sums to at most kOptMax
-// (so no element exceeds it, and O and l stay far inside the fp32 range).
-// A workgroup where some lane's sum does not runs its tiles again with the
-// max taken on every tile.  The reference is an actual score of the row, so
-// no element that matters can underflow.
-constexpr float kOptMax = 4294967296.f;   // 2^32
+// After its first two tiles the fast phase takes no row max (kOptMax, in
+// fa_fwd_short.h, bounds what it may then meet); a workgroup where a lane's
+// check fails runs its tiles again with the max taken on every tile.
 
 template <typename T, int D, int NW, int RB_, int KBN_>
 struct FwdCfg {

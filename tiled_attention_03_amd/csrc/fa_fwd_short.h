@@ -23,8 +23,10 @@
 //     (32 bytes per lane, lane t for tile t) and keeps, per lane, the
 //     valid-key bits of its tile; tiles without a valid key are never loaded.
 //   * Every tile takes the per-element rules (key flags, the causal rule,
-//     ALiBi) from those bits and its indices: the VALU work is small next to
-//     the loads.
+//     ALiBi) from those bits and its indices.  Without the causal rule and
+//     ALiBi, tiles past the first that sets the rows' running max take no max
+//     (the optimistic reference above); a wave where a lane's check fails
+//     computes its tiles again with the max on each.
 //
 // Tiles are visited from the first one up (the rows are positions 0..31, so
 // under ALiBi the nearest keys come first).  Handles
@@ -42,6 +44,14 @@ namespace fa {
 namespace {
 
 constexpr int kShortMaxTiles = 64;   // 32-key tiles the key-flag pass covers (one per lane)
+// Optimistic softmax reference (both forward kernels): once a row's running
+// max is set, later tiles may skip the max and keep the reference, as long as
+// every exponential stays <= 2^32 (then O and l stay far inside the fp32
+// range).  Each lane checks that its share of a tile's sum of exponentials is
+// at most kOptMax (so no element exceeds it); where one does not, the tiles
+// are computed again with the max taken on every tile.  The reference is an
+// actual score of the row, so no element that matters can underflow.
+constexpr float kOptMax = 4294967296.f;   // 2^32
 
 template <int D>
 struct ShortCfg {
@@ -174,11 +184,19 @@ __global__ __launch_bounds__(64, ShortCfg<D>::OCC) void fwd_short_kernel(Params 
   float m_run = -INFINITY, l_run = 0.f;
 
   // one tile: S^T = K Q^T from registers, the per-element rules, online
-  // softmax with the lazy rescale (the reference max moves only when a row's
-  // max grows by more than kShortTau), O^T += V^T P^T
+  // softmax, O^T += V^T P^T.  Safe form: the lazy rescale (the reference max
+  // moves only when a row's max grows by more than kShortTau).  Optimistic
+  // form (OPT, neither the causal rule nor ALiBi, once every row of the wave
+  // has a reference): no max, the reference stays, the key flags mask the
+  // exponentials, and bad flags a lane whose share of the tile's sum passes
+  // kOptMax.
   constexpr float kShortTau = 8.f;
-  auto compute = [&](auto slot, int t) __attribute__((always_inline)) {
+  bool bad = false;
+  auto compute = [&](auto slot, int t, auto opt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
+    // the optimistic form at D = 64 only: at D = 128 its registers do not fit
+    // two waves per SIMD without spills
+    constexpr bool OPT = decltype(opt)::value && D <= 64;
     const uint16_t *vs = S == 0 ? V0 : S == 1 ? V1 : V2;
     f32x16 s = f32x16{};
 #pragma unroll
@@ -186,38 +204,53 @@ __global__ __launch_bounds__(64, ShortCfg<D>::OCC) void fwd_short_kernel(Params 
     // element r holds key 32 t + c + 4 g, c = 8 (r / 4) + r % 4
     const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)kbits, t) >> (4 * g);
     const int dj = 32 * t + 4 * g - i;   // key - row of element c = 0
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 8 * (r >> 2) + (r & 3);
-      float x = s[r] * c_log2;
-      if (alibi) x -= sl2 * fabsf((float)(dj + c));
-      bool ok = (kb >> c) & 1u;
-      if (causal) ok = ok && dj + c <= 0;
-      x = ok ? x : -INFINITY;
-      s[r] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = max_lane_pair(mx);
-    const bool grow = mx > m_run + kShortTau;
-    float alpha = 1.f;
-    if (grow) {
-      alpha = exp2_fast(m_run - mx);
-      m_run = mx;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-    }
-    const float off = m_run == -INFINITY ? 0.f : m_run;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float alpha = 1.f;
+    if (OPT && !causal && !alibi && __all(m_run != -INFINITY)) {
+      // p = exp2(s c - m), kept where the key flag bit is set: the bit,
+      // sign-extended to 0 or all ones, masks p's bits (2 instructions)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = exp2_fast(s[r] - off);
-      s[r] = x;
-      part[r & 3] += x;
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        const float x = exp2_fast(fmaf(s[r], c_log2, -m_run));
+        const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)kb, c, 1);
+        s[r] = __uint_as_float(__float_as_uint(x) & keep);
+        part[r & 3] += s[r];
+      }
+    } else {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        float x = s[r] * c_log2;
+        if (alibi) x -= sl2 * fabsf((float)(dj + c));
+        bool ok = (kb >> c) & 1u;
+        if (causal) ok = ok && dj + c <= 0;
+        x = ok ? x : -INFINITY;
+        s[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = max_lane_pair(mx);
+      const bool grow = mx > m_run + kShortTau;
+      if (grow) {
+        alpha = exp2_fast(m_run - mx);
+        m_run = mx;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      const float off = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = exp2_fast(s[r] - off);
+        s[r] = x;
+        part[r & 3] += x;
+      }
     }
-    l_run = l_run * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
+    const float tsum = (part[0] + part[1]) + (part[2] + part[3]);
+    l_run = l_run * alpha + tsum;
+    if (OPT) bad |= tsum > kOptMax;
     u32x4 pk[2];
     pk[0] = pack8<T>(s, 0);
     pk[1] = pack8<T>(s, 8);
@@ -248,21 +281,42 @@ __global__ __launch_bounds__(64, ShortCfg<D>::OCC) void fwd_short_kernel(Params 
   // reads.  The loop runs whole rounds of NS steps with no exit inside a
   // round (steps past the last tile only issue and wait), so every step sees
   // the same loads in flight.
-  auto step = [&](auto slot) __attribute__((always_inline)) {
+  auto step = [&](auto slot, auto opt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
     constexpr int SN = (S + P) % NS;
     tq[SN] = pop();
     issue_tile(BufIdx<SN>{}, tq[SN]);
     wait_vm(std::integral_constant<int, P * C::LPT>{});
-    if (tq[S] >= 0) compute(BufIdx<S>{}, tq[S]);
+    if (tq[S] >= 0) compute(BufIdx<S>{}, tq[S], opt);
   };
   static_assert(NS == 3, "the loop below names three slots");
+  const uint64_t rem0 = rem;
   for (int n = 0; n < n_tiles; n += NS) {
-    step(BufIdx<0>{});
-    step(BufIdx<1>{});
-    step(BufIdx<2>{});
+    step(BufIdx<0>{}, std::true_type{});
+    step(BufIdx<1>{}, std::true_type{});
+    step(BufIdx<2>{}, std::true_type{});
   }
   wait_vm(std::integral_constant<int, 0>{});   // no load into LDS outlives the workgroup
+  if (__any(bad)) {
+    // an exponential of the optimistic pass reached kOptMax: every tile
+    // again, the row max taken on each
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    rem = rem0;
+    tq[0] = nt > 0 ? 0 : -1;
+    tq[1] = nt > 1 ? 1 : -1;
+    tq[2] = -1;
+    issue_tile(BufIdx<0>{}, tq[0]);
+    issue_tile(BufIdx<1>{}, tq[1]);
+    for (int n = 0; n < n_tiles; n += NS) {
+      step(BufIdx<0>{}, std::false_type{});
+      step(BufIdx<1>{}, std::false_type{});
+      step(BufIdx<2>{}, std::false_type{});
+    }
+    wait_vm(std::integral_constant<int, 0>{});
+  }
 
   // epilogue: O = acc / l, LSE
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
