@@ -312,7 +312,7 @@ def test_large_scores_exercise_running_max(D):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("mask", ["none", "causal+alibi"])
+@pytest.mark.parametrize("mask", ["none", "causal+alibi", "alibi"])
 def test_score_spike_in_a_late_tile(D, dtype, mask):
     """One key of head 0 (key 3, in the tile the forward visits last outside
     the causal band) scores about 180 base-2 units above every other key of
